@@ -1,0 +1,77 @@
+"""Builds libbsx.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+Each source compiles to an object in parallel under ``_build/``; the objects link
+into ``block_sparse_cross_amd/libbsx.so``, replaced atomically so a process that
+already loaded the previous library is not disturbed.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB_PATH = os.path.join(PKG, "libbsx.so")
+
+SOURCES = [
+    "api.cpp",
+    "upload.hip",
+    "cost.hip",
+    "lse_merge.hip",
+    "fwd_f32.hip",
+    "fwd_bf16.hip",
+    "bwd_bf16.hip",
+]
+
+ARCH = "gfx950"
+# Packed f32 VALU forms stay disabled in every HIP object.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
+                "-Wall", "-Wno-unused-function"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; libbsx needs ROCm's hipcc to build")
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [_hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
+                    if "packed-fp32-ops" not in line and line.strip())
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{out}")
+    if verbose and out:
+        print(out, flush=True)
+    return obj
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source for gfx950 and link libbsx.so; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB_PATH + f".tmp{os.getpid()}"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,422 @@
+// Host side of libbsx: argument checks, LPT planning, per-call work descriptors,
+// and kernel launches.  Every entry point validates all of its arguments before
+// touching the HIP runtime, so argument errors never launch anything.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "../../include/bsx.h"
+#include "bsx_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bsx_status fail(bsx_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bsx_status ok() {
+  g_last_error.clear();
+  return BSX_OK;
+}
+
+bsx_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BSX_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kMaxBlockSize = 256;
+constexpr int kHeadDim = 128;
+
+// Checks the fields every attention call relies on.
+bsx_status check_shape(const bsx_shape* s, bool need_heads) {
+  if (!s) return fail(BSX_E_INVALID, "shape is NULL");
+  if (s->n_blocks < 0) return fail(BSX_E_INVALID, "n_blocks = %d < 0", s->n_blocks);
+  if (s->block_size < 1 || s->block_size > kMaxBlockSize)
+    return fail(BSX_E_INVALID, "block_size = %d outside [1, %d]", s->block_size, kMaxBlockSize);
+  if (s->ctx_len < 0) return fail(BSX_E_INVALID, "ctx_len = %lld < 0", (long long)s->ctx_len);
+  if (s->ctx_len > (int64_t(1) << 40))
+    return fail(BSX_E_INVALID, "ctx_len = %lld exceeds 2^40", (long long)s->ctx_len);
+  if ((int64_t)s->n_blocks * s->block_size > (int64_t(1) << 24))
+    return fail(BSX_E_INVALID, "n_blocks * block_size exceeds 2^24 queries");
+  if (!need_heads) return ok();
+  if (s->n_kv_heads < 1) return fail(BSX_E_INVALID, "n_kv_heads = %d < 1", s->n_kv_heads);
+  if (s->n_q_heads < s->n_kv_heads || s->n_q_heads % s->n_kv_heads != 0)
+    return fail(BSX_E_INVALID, "n_q_heads = %d is not a positive multiple of n_kv_heads = %d",
+                s->n_q_heads, s->n_kv_heads);
+  if (s->n_q_heads > 1024) return fail(BSX_E_INVALID, "n_q_heads = %d > 1024", s->n_q_heads);
+  if (s->dtype != BSX_F32 && s->dtype != BSX_BF16)
+    return fail(BSX_E_INVALID, "dtype = %d is not BSX_F32 or BSX_BF16", s->dtype);
+  if (s->head_dim < 1) return fail(BSX_E_INVALID, "head_dim = %d < 1", s->head_dim);
+  if (s->head_dim != kHeadDim)
+    return fail(BSX_E_UNSUPPORTED, "head_dim = %d (only %d is implemented)", s->head_dim,
+                kHeadDim);
+  if (!std::isfinite(s->scale)) return fail(BSX_E_INVALID, "scale is not finite");
+  return ok();
+}
+
+// Checks a chunk table; on success *n_local is the local K/V length.
+bsx_status check_chunks(const bsx_shape* s, const bsx_chunks* c, bool need_slots,
+                        int64_t* n_local) {
+  if (!c) return fail(BSX_E_INVALID, "chunks is NULL");
+  if (c->n_chunks < 0) return fail(BSX_E_INVALID, "n_chunks = %d < 0", c->n_chunks);
+  if (c->n_chunks > (1 << 20)) return fail(BSX_E_INVALID, "n_chunks = %d > 2^20", c->n_chunks);
+  if (c->n_chunks > 0 && (!c->start || !c->len))
+    return fail(BSX_E_INVALID, "chunk start/len arrays are NULL");
+  int64_t total = 0;
+  for (int32_t i = 0; i < c->n_chunks; ++i) {
+    const int64_t st = c->start[i], ln = c->len[i];
+    if (ln < 0) return fail(BSX_E_INVALID, "chunk %d: len = %lld < 0", i, (long long)ln);
+    if (st < 0 || st > s->ctx_len || ln > s->ctx_len - st)
+      return fail(BSX_E_INVALID, "chunk %d: [%lld, %lld) is not inside [0, %lld)", i,
+                  (long long)st, (long long)(st + ln), (long long)s->ctx_len);
+    total += ln;
+  }
+  if (need_slots) {
+    if (c->n_slots < (c->n_chunks > 0 ? 1 : 0) || c->n_slots > (1 << 20))
+      return fail(BSX_E_INVALID, "n_slots = %d is out of range", c->n_slots);
+    if (!c->slot) {
+      if (c->n_slots != c->n_chunks)
+        return fail(BSX_E_INVALID, "slot is NULL but n_slots (%d) != n_chunks (%d)", c->n_slots,
+                    c->n_chunks);
+    } else {
+      for (int32_t i = 0; i < c->n_chunks; ++i)
+        if (c->slot[i] < 0 || c->slot[i] >= c->n_slots)
+          return fail(BSX_E_INVALID, "chunk %d: slot %d outside [0, %d)", i, c->slot[i],
+                      c->n_slots);
+    }
+  }
+  if (n_local) *n_local = total;
+  return ok();
+}
+
+// Per-call descriptor of the forward pass: slot_ptr[n_slots + 1] (int32), then the
+// non-empty chunks grouped by slot in chunk index order (ChunkEntry, 8-byte aligned).
+struct FwdLayout {
+  size_t ptr_bytes;
+  size_t entries_off;
+  size_t total;
+};
+
+FwdLayout fwd_layout(int32_t n_slots, int32_t n_chunks) {
+  FwdLayout l;
+  l.ptr_bytes = sizeof(int32_t) * (size_t(n_slots) + 1);
+  l.entries_off = align_up(l.ptr_bytes, 8);
+  l.total = l.entries_off + sizeof(bsx::ChunkEntry) * size_t(n_chunks);
+  return l;
+}
+
+void build_fwd_descriptor(const bsx_chunks* c, std::vector<uint32_t>* words, int32_t* n_entries) {
+  const int32_t nc = c->n_chunks, ns = c->n_slots;
+  const FwdLayout l = fwd_layout(ns, nc);
+  std::vector<int64_t> off(nc);
+  int64_t acc = 0;
+  for (int32_t i = 0; i < nc; ++i) {
+    off[i] = acc;
+    acc += c->len[i];
+  }
+  std::vector<int32_t> count(ns + 1, 0);
+  for (int32_t i = 0; i < nc; ++i)
+    if (c->len[i] > 0) count[(c->slot ? c->slot[i] : i) + 1]++;
+  std::vector<int32_t> ptr(ns + 1, 0);
+  for (int32_t s = 0; s < ns; ++s) ptr[s + 1] = ptr[s] + count[s + 1];
+  std::vector<bsx::ChunkEntry> ent(ptr[ns]);
+  std::vector<int32_t> fill(ptr.begin(), ptr.end() - 1);
+  for (int32_t i = 0; i < nc; ++i) {
+    if (c->len[i] <= 0) continue;
+    const int32_t s = c->slot ? c->slot[i] : i;
+    ent[fill[s]++] = bsx::ChunkEntry{c->start[i], c->len[i], off[i]};
+  }
+  const size_t used = l.entries_off + sizeof(bsx::ChunkEntry) * ent.size();
+  words->assign(align_up(used, 4) / 4, 0u);
+  std::memcpy(words->data(), ptr.data(), l.ptr_bytes);
+  if (!ent.empty())
+    std::memcpy(reinterpret_cast<char*>(words->data()) + l.entries_off, ent.data(),
+                sizeof(bsx::ChunkEntry) * ent.size());
+  *n_entries = ptr[ns];
+}
+
+float resolve_scale(const bsx_shape* s) {
+  return s->scale > 0.f ? s->scale : 1.0f / std::sqrt(float(s->head_dim));
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+int bsx_abi_version(void) { return BSX_ABI_VERSION; }
+
+const char* bsx_last_error(void) { return g_last_error.c_str(); }
+
+const char* bsx_status_string(int status) {
+  switch (status) {
+    case BSX_OK: return "BSX_OK";
+    case BSX_E_INVALID: return "BSX_E_INVALID";
+    case BSX_E_UNSUPPORTED: return "BSX_E_UNSUPPORTED";
+    case BSX_E_WORKSPACE: return "BSX_E_WORKSPACE";
+    case BSX_E_DEVICE: return "BSX_E_DEVICE";
+    default: return "unknown bsx_status";
+  }
+}
+
+bsx_status bsx_validate_mask(const bsx_shape* shape, const int64_t* anchor,
+                             const int64_t* ctx_begin) {
+  bsx_status st = check_shape(shape, false);
+  if (st != BSX_OK) return st;
+  if (shape->n_blocks > 0 && (!anchor || !ctx_begin))
+    return fail(BSX_E_INVALID, "anchor/ctx_begin is NULL");
+  for (int32_t b = 0; b < shape->n_blocks; ++b) {
+    const int64_t lo = ctx_begin[b], hi = anchor[b];
+    if (lo < 0 || lo > hi || hi > shape->ctx_len)
+      return fail(BSX_E_INVALID, "block %d: context range [%lld, %lld) is not inside [0, %lld]",
+                  b, (long long)lo, (long long)hi, (long long)shape->ctx_len);
+  }
+  return ok();
+}
+
+bsx_status bsx_lpt(int32_t n_items, const int64_t* cost, int32_t n_bins, int32_t* bin_of,
+                   int64_t* bin_load, int64_t* makespan, double* imbalance) {
+  if (n_items < 0) return fail(BSX_E_INVALID, "n_items = %d < 0", n_items);
+  if (n_bins < 1) return fail(BSX_E_INVALID, "n_bins = %d < 1", n_bins);
+  if (n_items > 0 && (!cost || !bin_of)) return fail(BSX_E_INVALID, "cost/bin_of is NULL");
+  for (int32_t i = 0; i < n_items; ++i)
+    if (cost[i] < 0) return fail(BSX_E_INVALID, "cost[%d] = %lld < 0", i, (long long)cost[i]);
+  std::vector<int32_t> order(n_items);
+  std::iota(order.begin(), order.end(), 0);
+  std::sort(order.begin(), order.end(), [cost](int32_t a, int32_t b) {
+    return cost[a] != cost[b] ? cost[a] > cost[b] : a < b;
+  });
+  std::vector<int64_t> load(n_bins, 0);
+  int64_t total = 0;
+  for (int32_t i : order) {
+    int32_t best = 0;
+    for (int32_t j = 1; j < n_bins; ++j)
+      if (load[j] < load[best]) best = j;  // strict: ties keep the lower index
+    bin_of[i] = best;
+    load[best] += cost[i];
+    total += cost[i];
+  }
+  const int64_t ms = *std::max_element(load.begin(), load.end());
+  if (bin_load) std::copy(load.begin(), load.end(), bin_load);
+  if (makespan) *makespan = ms;
+  if (imbalance)
+    *imbalance = total > 0 ? double(ms) / (double(total) / double(n_bins)) - 1.0 : 0.0;
+  return ok();
+}
+
+size_t bsx_cost_workspace(int32_t n_chunks) {
+  return align_up(sizeof(int64_t) * 2 * size_t(n_chunks < 0 ? 0 : n_chunks), 256) + 256;
+}
+
+bsx_status bsx_cost(const bsx_shape* shape, const int64_t* anchor, const int64_t* ctx_begin,
+                    const bsx_chunks* chunks, int64_t* counts, int64_t* chunk_cost,
+                    int32_t* mask_err, void* ws, size_t ws_bytes, void* stream) {
+  bsx_status st = check_shape(shape, false);
+  if (st != BSX_OK) return st;
+  st = check_chunks(shape, chunks, false, nullptr);
+  if (st != BSX_OK) return st;
+  if (!mask_err) return fail(BSX_E_INVALID, "mask_err is NULL");
+  if (shape->n_blocks > 0 && (!anchor || !ctx_begin))
+    return fail(BSX_E_INVALID, "anchor/ctx_begin is NULL");
+  if (chunks->n_chunks > 0 && !chunk_cost) return fail(BSX_E_INVALID, "chunk_cost is NULL");
+  const size_t need = bsx_cost_workspace(chunks->n_chunks);
+  if (!ws || ws_bytes < need)
+    return fail(BSX_E_WORKSPACE, "workspace of %zu bytes is smaller than %zu", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<uint32_t> words(size_t(chunks->n_chunks) * 4);
+  for (int32_t i = 0; i < chunks->n_chunks; ++i) {
+    const int64_t se[2] = {chunks->start[i], chunks->len[i]};
+    std::memcpy(&words[size_t(i) * 4], se, sizeof(se));
+  }
+  hipError_t e = bsx::launch_upload(words.data(), words.size(), static_cast<uint32_t*>(ws), s);
+  if (e != hipSuccess) return device_status(e, "cost descriptor upload");
+  bsx::CostParams p{};
+  p.anchor = anchor;
+  p.ctx_begin = ctx_begin;
+  p.chunk_se = static_cast<const int64_t*>(ws);
+  p.counts = counts;
+  p.chunk_cost = chunk_cost;
+  p.mask_err = mask_err;
+  p.ctx_len = shape->ctx_len;
+  p.n_blocks = shape->n_blocks;
+  p.block_size = shape->block_size;
+  p.n_chunks = chunks->n_chunks;
+  return device_status(bsx::launch_cost(p, s), "cost kernel");
+}
+
+size_t bsx_fwd_workspace(const bsx_shape* shape, const bsx_chunks* chunks) {
+  (void)shape;
+  if (!chunks || chunks->n_chunks < 0 || chunks->n_slots < 0) return 0;
+  return align_up(fwd_layout(chunks->n_slots, chunks->n_chunks).total, 256);
+}
+
+bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, const void* v,
+                        const void* k_self, const void* v_self, const int64_t* anchor,
+                        const int64_t* ctx_begin, const bsx_chunks* chunks, float* o_part,
+                        float* lse_part, void* ws, size_t ws_bytes, void* stream) {
+  bsx_status st = check_shape(shape, true);
+  if (st != BSX_OK) return st;
+  int64_t n_local = 0;
+  st = check_chunks(shape, chunks, true, &n_local);
+  if (st != BSX_OK) return st;
+  if ((k_self == nullptr) != (v_self == nullptr))
+    return fail(BSX_E_INVALID, "k_self and v_self must both be given or both be NULL");
+  const int has_self = k_self != nullptr;
+  const int64_t n_out = int64_t(chunks->n_slots) + has_self;
+  if (shape->n_blocks == 0 || n_out == 0) return ok();
+  if (!q || !anchor || !ctx_begin || !o_part || !lse_part)
+    return fail(BSX_E_INVALID, "q/anchor/ctx_begin/o_part/lse_part is NULL");
+  if (n_local > 0 && (!k || !v)) return fail(BSX_E_INVALID, "k/v is NULL");
+  const size_t need = bsx_fwd_workspace(shape, chunks);
+  if (!ws || ws_bytes < need)
+    return fail(BSX_E_WORKSPACE, "workspace of %zu bytes is smaller than %zu", ws_bytes, need);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<uint32_t> words;
+  int32_t n_entries = 0;
+  build_fwd_descriptor(chunks, &words, &n_entries);
+  hipError_t e = bsx::launch_upload(words.data(), words.size(), static_cast<uint32_t*>(ws), s);
+  if (e != hipSuccess) return device_status(e, "forward descriptor upload");
+  const FwdLayout l = fwd_layout(chunks->n_slots, chunks->n_chunks);
+
+  bsx::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.k_self = k_self;
+  p.v_self = v_self;
+  p.anchor = anchor;
+  p.ctx_begin = ctx_begin;
+  p.slot_ptr = static_cast<const int32_t*>(ws);
+  p.entries = reinterpret_cast<const bsx::ChunkEntry*>(static_cast<const char*>(ws) +
+                                                        l.entries_off);
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.ctx_len = shape->ctx_len;
+  p.n_local = n_local;
+  p.n_blocks = shape->n_blocks;
+  p.block_size = shape->block_size;
+  p.n_q_heads = shape->n_q_heads;
+  p.n_kv_heads = shape->n_kv_heads;
+  p.n_slots = chunks->n_slots;
+  p.has_self = has_self;
+  p.scale = resolve_scale(shape);
+  p.scale_log2 = p.scale * kLog2e;
+  e = shape->dtype == BSX_BF16 ? bsx::launch_fwd_bf16(p, s) : bsx::launch_fwd_f32(p, s);
+  return device_status(e, "forward kernel");
+}
+
+bsx_status bsx_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
+                         const float* o_parts, const float* lse_parts, float* o_out,
+                         float* lse_out, void* stream) {
+  if (n_parts < 1 || n_parts > 4096)
+    return fail(BSX_E_INVALID, "n_parts = %d outside [1, 4096]", n_parts);
+  if (n_rows < 0) return fail(BSX_E_INVALID, "n_rows = %lld < 0", (long long)n_rows);
+  if (head_dim < 4 || head_dim > 512 || head_dim % 4 != 0)
+    return fail(BSX_E_INVALID, "head_dim = %d is not a multiple of 4 in [4, 512]", head_dim);
+  if (n_rows == 0) return ok();
+  if (!o_parts || !lse_parts || !o_out || !lse_out)
+    return fail(BSX_E_INVALID, "a merge pointer is NULL");
+  return device_status(bsx::launch_lse_merge(n_parts, n_rows, head_dim, o_parts, lse_parts,
+                                             o_out, lse_out, static_cast<hipStream_t>(stream)),
+                       "merge kernel");
+}
+
+size_t bsx_bwd_workspace(const bsx_shape* shape, const bsx_chunks* chunks) {
+  if (!shape || !chunks || chunks->n_chunks < 0 || shape->n_blocks < 0 || shape->block_size < 0 ||
+      shape->n_q_heads < 0)
+    return 0;
+  const size_t ent = align_up(sizeof(bsx::ChunkEntry) * size_t(chunks->n_chunks), 256);
+  const size_t delta =
+      align_up(sizeof(float) * size_t(shape->n_blocks) * shape->block_size * shape->n_q_heads, 256);
+  return ent + delta + 256;
+}
+
+bsx_status bsx_attn_bwd(const bsx_shape* shape, const void* q, const void* k, const void* v,
+                        const void* k_self, const void* v_self, const float* o,
+                        const float* lse, const void* d_o, const int64_t* anchor,
+                        const int64_t* ctx_begin, const bsx_chunks* chunks, float* dq,
+                        float* dk, float* dv, float* dk_self, float* dv_self, void* ws,
+                        size_t ws_bytes, void* stream) {
+  bsx_status st = check_shape(shape, true);
+  if (st != BSX_OK) return st;
+  int64_t n_local = 0;
+  st = check_chunks(shape, chunks, false, &n_local);
+  if (st != BSX_OK) return st;
+  if (shape->dtype != BSX_BF16)
+    return fail(BSX_E_UNSUPPORTED, "the backward pass takes bf16 inputs only");
+  if ((k_self == nullptr) != (v_self == nullptr))
+    return fail(BSX_E_INVALID, "k_self and v_self must both be given or both be NULL");
+  const int has_self = k_self != nullptr;
+  if (has_self && (!dk_self || !dv_self))
+    return fail(BSX_E_INVALID, "dk_self/dv_self is NULL while k_self is given");
+  if (shape->n_blocks > 0 && (!q || !o || !lse || !d_o || !anchor || !ctx_begin || !dq))
+    return fail(BSX_E_INVALID, "q/o/lse/d_o/anchor/ctx_begin/dq is NULL");
+  if (n_local > 0 && (!k || !v || !dk || !dv)) return fail(BSX_E_INVALID, "k/v/dk/dv is NULL");
+  const size_t need = bsx_bwd_workspace(shape, chunks);
+  if (!ws || ws_bytes < need)
+    return fail(BSX_E_WORKSPACE, "workspace of %zu bytes is smaller than %zu", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // local offsets of the non-empty chunks, in chunk index order
+  std::vector<bsx::ChunkEntry> ent;
+  int64_t acc = 0;
+  for (int32_t i = 0; i < chunks->n_chunks; ++i) {
+    if (chunks->len[i] > 0) ent.push_back(bsx::ChunkEntry{chunks->start[i], chunks->len[i], acc});
+    acc += chunks->len[i];
+  }
+  std::vector<uint32_t> words(ent.size() * sizeof(bsx::ChunkEntry) / 4);
+  if (!ent.empty()) std::memcpy(words.data(), ent.data(), ent.size() * sizeof(bsx::ChunkEntry));
+  hipError_t e = bsx::launch_upload(words.data(), words.size(), static_cast<uint32_t*>(ws), s);
+  if (e != hipSuccess) return device_status(e, "backward descriptor upload");
+  const size_t ent_bytes = align_up(sizeof(bsx::ChunkEntry) * size_t(chunks->n_chunks), 256);
+  bsx::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.k_self = k_self;
+  p.v_self = v_self;
+  p.o = o;
+  p.lse = lse;
+  p.d_o = d_o;
+  p.anchor = anchor;
+  p.ctx_begin = ctx_begin;
+  p.entries = static_cast<const bsx::ChunkEntry*>(ws);
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dk_self = dk_self;
+  p.dv_self = dv_self;
+  p.delta = reinterpret_cast<float*>(static_cast<char*>(ws) + ent_bytes);
+  p.ctx_len = shape->ctx_len;
+  p.n_local = n_local;
+  p.n_entries = int32_t(ent.size());
+  p.n_blocks = shape->n_blocks;
+  p.block_size = shape->block_size;
+  p.n_q_heads = shape->n_q_heads;
+  p.n_kv_heads = shape->n_kv_heads;
+  p.has_self = has_self;
+  p.scale = resolve_scale(shape);
+  p.scale_log2 = p.scale * kLog2e;
+  return device_status(bsx::launch_bwd_bf16(p, s), "backward kernels");
+}
+
+}  // extern "C"

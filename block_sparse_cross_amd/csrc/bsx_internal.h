@@ -1,0 +1,100 @@
+// Internal declarations shared by the host API (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bsx {
+
+// One non-empty KV chunk as the attention kernels see it: packed positions
+// [start, start + len) stored at local rows [local_off, local_off + len).
+struct ChunkEntry {
+  int64_t start;
+  int64_t len;
+  int64_t local_off;
+};
+
+// Forward problem as handed to the kernels.  Entries are grouped by output slot:
+// slot s owns entries [slot_ptr[s], slot_ptr[s + 1]), in chunk index order.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* k_self;
+  const void* v_self;
+  const int64_t* anchor;
+  const int64_t* ctx_begin;
+  const int32_t* slot_ptr;
+  const ChunkEntry* entries;
+  float* o_part;
+  float* lse_part;
+  int64_t ctx_len;
+  int64_t n_local;
+  int32_t n_blocks;
+  int32_t block_size;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t n_slots;    // context slots; the self slot, when present, is index n_slots
+  int32_t has_self;
+  float scale;        // softmax scale
+  float scale_log2;   // scale * log2(e)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* k_self;
+  const void* v_self;
+  const float* o;
+  const float* lse;
+  const void* d_o;
+  const int64_t* anchor;
+  const int64_t* ctx_begin;
+  const ChunkEntry* entries;  // every non-empty chunk, in chunk index order
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dk_self;
+  float* dv_self;
+  float* delta;               // workspace [N_q][H_q]: rowsum(dO * O)
+  int64_t ctx_len;
+  int64_t n_local;
+  int32_t n_entries;
+  int32_t n_blocks;
+  int32_t block_size;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t has_self;
+  float scale;
+  float scale_log2;
+};
+
+struct CostParams {
+  const int64_t* anchor;
+  const int64_t* ctx_begin;
+  const int64_t* chunk_se;  // [n_chunks][2]: start, len
+  int64_t* counts;          // may be null
+  int64_t* chunk_cost;
+  int32_t* mask_err;
+  int64_t ctx_len;
+  int32_t n_blocks;
+  int32_t block_size;
+  int32_t n_chunks;
+};
+
+// Largest payload one upload launch carries in its kernel arguments.
+constexpr int kUploadWords = 480;
+
+hipError_t launch_upload(const uint32_t* host_words, size_t n_words, uint32_t* dst,
+                         hipStream_t stream);
+hipError_t launch_cost(const CostParams& p, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
+hipError_t launch_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
+                            const float* o_parts, const float* lse_parts, float* o_out,
+                            float* lse_out, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+
+}  // namespace bsx

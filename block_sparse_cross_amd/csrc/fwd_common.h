@@ -1,0 +1,85 @@
+// Device helpers shared by the forward attention kernels: the visibility rule
+// and the walk over a slot's key segments.
+//
+// Visibility (Split-KV page, Abstract: anchor-sampled draft blocks cross-attend
+// the context under a block-sparse mask): the queries of block b see the context
+// positions [ctx_begin[b], anchor[b]) and the B keys of their own draft block.
+// In the self slot, "positions" are draft-key rows, so block b sees [b*B, b*B+B).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "bsx_internal.h"
+
+namespace bsx {
+
+// Visible range of block `blk` in the slot's position space, clamped to [0, S].
+__device__ inline void visible_range(const FwdParams& p, bool self_slot, int64_t blk,
+                                     int64_t* lo, int64_t* hi) {
+  if (self_slot) {
+    *lo = blk * p.block_size;
+    *hi = *lo + p.block_size;
+    return;
+  }
+  int64_t a = p.ctx_begin[blk], z = p.anchor[blk];
+  a = a < 0 ? 0 : (a > p.ctx_len ? p.ctx_len : a);
+  z = z < a ? a : (z > p.ctx_len ? p.ctx_len : z);
+  *lo = a;
+  *hi = z;
+}
+
+// Walks the key segments a workgroup must visit for one slot: each segment is a
+// run of positions [seg0, seg1) stored at local rows local0 .. local0 + (seg1 - seg0),
+// already cut to the union [minlo, maxhi) of the ranges its rows can see.
+struct SegmentWalk {
+  const ChunkEntry* ent;
+  int e;
+  int e_end;
+  int64_t minlo;
+  int64_t maxhi;
+  bool self_slot;
+  int64_t seg0;
+  int64_t seg1;
+  int64_t local0;
+
+  __device__ void init(const FwdParams& p, int slot, bool is_self, int64_t lo, int64_t hi) {
+    self_slot = is_self;
+    minlo = lo;
+    maxhi = hi;
+    if (is_self) {
+      ent = nullptr;
+      e = 0;
+      e_end = 1;
+    } else {
+      ent = p.entries;
+      e = p.slot_ptr[slot];
+      e_end = p.slot_ptr[slot + 1];
+    }
+  }
+
+  // Advances to the next non-empty segment; false when the slot is exhausted.
+  __device__ bool next() {
+    if (self_slot) {
+      if (e >= e_end) return false;
+      e = e_end;
+      seg0 = minlo;
+      seg1 = maxhi;
+      local0 = minlo;
+      return seg0 < seg1;
+    }
+    while (e < e_end) {
+      const ChunkEntry c = ent[e++];
+      const int64_t a = c.start > minlo ? c.start : minlo;
+      const int64_t z = c.start + c.len < maxhi ? c.start + c.len : maxhi;
+      if (a < z) {
+        seg0 = a;
+        seg1 = z;
+        local0 = c.local_off + (a - c.start);
+        return true;
+      }
+    }
+    return false;
+  }
+};
+
+}  // namespace bsx

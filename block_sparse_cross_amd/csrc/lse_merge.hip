@@ -1,0 +1,138 @@
+// Exact merge of partial (O, LSE) pairs.
+//
+// Split-KV page, Abstract: the context-parallel method is exact while moving only
+// query-sized tensors.  With normalized partials the exact combination is
+//   LSE = M + log sum_p exp(LSE_p - M),   O = sum_p exp(LSE_p - LSE) O_p,
+// M = max_p LSE_p; partials with LSE_p = -inf are skipped without reading O_p.
+//
+// Bandwidth-bound: the kernel streams every finite partial row once.  A workgroup
+// owns kRowsPerWg consecutive rows.  Phase 1: the four waves split the partials,
+// each lane keeps an online (max, sum) for one row from coalesced LSE loads, and
+// the four partial sums meet in LDS.  Phase 2: head_dim/4 lanes per row each own
+// one float4 of the row and accumulate the weighted partial rows, with the part
+// loop unrolled so several 16-byte loads are in flight per lane.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "bsx_internal.h"
+
+namespace bsx {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerWg = 64;
+constexpr int kUnroll = 8;
+
+__global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_t n_rows,
+                                                             int head_dim,
+                                                             const float* __restrict__ o_parts,
+                                                             const float* __restrict__ lse_parts,
+                                                             float* __restrict__ o_out,
+                                                             float* __restrict__ lse_out) {
+  __shared__ float sh_m[4][kRowsPerWg];
+  __shared__ float sh_s[4][kRowsPerWg];
+  __shared__ float sh_lse[kRowsPerWg];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int64_t row0 = int64_t(blockIdx.x) * kRowsPerWg;
+
+  // Phase 1: online max/sum of exp over this wave's share of the partials.
+  {
+    const int64_t row = row0 + lane;
+    float m = -INFINITY, s = 0.f;
+    if (row < n_rows) {
+      for (int p = wave; p < n_parts; p += 4) {
+        const float x = lse_parts[int64_t(p) * n_rows + row];
+        if (x == -INFINITY) continue;
+        if (x > m) {
+          s = s * expf(m - x) + 1.f;
+          m = x;
+        } else {
+          s += expf(x - m);
+        }
+      }
+    }
+    sh_m[wave][lane] = m;
+    sh_s[wave][lane] = s;
+  }
+  __syncthreads();
+  if (tid < kRowsPerWg) {
+    float m = -INFINITY;
+    for (int w = 0; w < 4; ++w) m = fmaxf(m, sh_m[w][tid]);
+    float lse = -INFINITY;
+    if (m != -INFINITY) {
+      float s = 0.f;
+      for (int w = 0; w < 4; ++w)
+        if (sh_m[w][tid] != -INFINITY) s += sh_s[w][tid] * expf(sh_m[w][tid] - m);
+      lse = m + logf(s);
+    }
+    sh_lse[tid] = lse;
+    const int64_t row = row0 + tid;
+    if (row < n_rows) lse_out[row] = lse;
+  }
+  __syncthreads();
+
+  // Phase 2: weighted sum of the finite partial rows.
+  const int tpr = head_dim >> 2;              // lanes per row, one float4 each
+  const int rows_per_pass = kThreads / tpr;
+  const int sub = tid / tpr, col = (tid % tpr) * 4;
+  if (sub >= rows_per_pass) return;
+  for (int r = sub; r < kRowsPerWg; r += rows_per_pass) {
+    const int64_t row = row0 + r;
+    if (row >= n_rows) break;
+    const float lse = sh_lse[r];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lse != -INFINITY) {
+      const float* lp = lse_parts + row;
+      const float* op = o_parts + row * head_dim + col;
+      const int64_t lstride = n_rows, ostride = n_rows * int64_t(head_dim);
+      int p = 0;
+      for (; p + kUnroll <= n_parts; p += kUnroll) {
+        float w[kUnroll];
+        float4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const float x = lp[int64_t(p + u) * lstride];
+          w[u] = 0.f;
+          v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (x != -INFINITY) {
+            w[u] = expf(x - lse);
+            v[u] = *reinterpret_cast<const float4*>(op + int64_t(p + u) * ostride);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          acc.x = fmaf(w[u], v[u].x, acc.x);
+          acc.y = fmaf(w[u], v[u].y, acc.y);
+          acc.z = fmaf(w[u], v[u].z, acc.z);
+          acc.w = fmaf(w[u], v[u].w, acc.w);
+        }
+      }
+      for (; p < n_parts; ++p) {
+        const float x = lp[int64_t(p) * lstride];
+        if (x == -INFINITY) continue;
+        const float w = expf(x - lse);
+        const float4 v = *reinterpret_cast<const float4*>(op + int64_t(p) * ostride);
+        acc.x = fmaf(w, v.x, acc.x);
+        acc.y = fmaf(w, v.y, acc.y);
+        acc.z = fmaf(w, v.z, acc.z);
+        acc.w = fmaf(w, v.w, acc.w);
+      }
+    }
+    *reinterpret_cast<float4*>(o_out + row * head_dim + col) = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
+                            const float* o_parts, const float* lse_parts, float* o_out,
+                            float* lse_out, hipStream_t stream) {
+  const int64_t blocks = (n_rows + kRowsPerWg - 1) / kRowsPerWg;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, n_parts,
+                     n_rows, head_dim, o_parts, lse_parts, o_out, lse_out);
+  return hipGetLastError();
+}
+
+}  // namespace bsx

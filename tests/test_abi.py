@@ -1,0 +1,167 @@
+"""The C ABI without a GPU: the library loads, exports every function include/bsx.h declares,
+its host-only entry points match the oracle bit for bit, and device entry points reject bad
+arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_cross_amd as bsx
+import oracle
+from block_sparse_cross_amd._lib import (BSX_E_INVALID, BSX_E_UNSUPPORTED, BSX_E_WORKSPACE,
+                                         BsxChunks, BsxShape, lib)
+from workloads import CONFIGS, make_workload
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "bsx.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsx_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 12
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.bsx_abi_version() == 1
+
+
+def test_status_strings():
+    L = lib()
+    assert L.bsx_status_string(0) == b"BSX_OK"
+    assert L.bsx_status_string(3) == b"BSX_E_WORKSPACE"
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_lpt_matches_oracle_on_workload_costs(idx):
+    wl = make_workload(CONFIGS[idx])
+    _, cost = oracle.chunk_costs(wl.anchor, wl.ctx_begin, wl.cfg.block_size, wl.chunk_start,
+                                 wl.chunk_len)
+    got = bsx.lpt(cost, wl.cfg.n_bins)
+    bin_of, loads, ms, imb = oracle.lpt(cost, wl.cfg.n_bins)
+    assert got.bin_of.tolist() == bin_of
+    assert got.loads.tolist() == loads
+    assert got.makespan == ms
+    assert got.imbalance == pytest.approx(imb, abs=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_lpt_matches_oracle_random(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(0, 300))
+    P = int(rng.integers(1, 70))
+    cost = rng.integers(0, 50 if seed % 3 else 5, size=n) * int(rng.integers(1, 1 << 30))
+    got = bsx.lpt(cost, P)
+    bin_of, loads, ms, imb = oracle.lpt(cost, P)
+    assert got.bin_of.tolist() == bin_of
+    assert got.loads.tolist() == loads and got.makespan == ms
+    assert got.imbalance == pytest.approx(imb, abs=1e-12)
+
+
+def test_lpt_rejects_bad_arguments():
+    with pytest.raises(bsx.BsxError):
+        bsx.lpt([1, 2], 0)
+    with pytest.raises(bsx.BsxError):
+        bsx.lpt([1, -1], 2)
+
+
+def test_validate_mask_matches_oracle():
+    shape = bsx.Shape(n_blocks=3, block_size=4, n_q_heads=4, n_kv_heads=2, ctx_len=50)
+    cases = [([10, 50, 0], [0, 20, 0]), ([10, 51, 0], [0, 20, 0]), ([10, 5, 0], [0, 20, 0]),
+             ([10, 50, 0], [-1, 20, 0])]
+    for an, be in cases:
+        bad = oracle.mask_error(an, be, 50)
+        if bad:
+            with pytest.raises(bsx.BsxError) as e:
+                bsx.validate_mask(shape, an, be)
+            assert e.value.status == BSX_E_INVALID
+        else:
+            bsx.validate_mask(shape, an, be)
+
+
+def _shape(**kw):
+    base = dict(n_blocks=2, block_size=16, n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1,
+                ctx_len=1024, scale=0.0)
+    base.update(kw)
+    return BsxShape(**base)
+
+
+def _chunks(start, length, slot=None, n_slots=None):
+    c = bsx.Chunks(start, length, slot, n_slots)
+    return c, c.c()
+
+
+def _fwd(shape, chunks_c, ws_bytes=1 << 20):
+    # Only called with arguments that fail validation: nothing is launched, so the
+    # placeholder pointers are never dereferenced.
+    f = ctypes.c_void_p(0x1000)
+    return lib().bsx_attn_fwd(ctypes.byref(shape), f, f, f, f, f, f, f, ctypes.byref(chunks_c),
+                              f, f, f, ws_bytes, None)
+
+
+def test_forward_rejects_bad_arguments_without_launching():
+    cc_keep, cc = _chunks([0, 512], [512, 512])
+    assert _fwd(_shape(head_dim=64), cc) == BSX_E_UNSUPPORTED
+    assert _fwd(_shape(n_q_heads=6, n_kv_heads=4), cc) == BSX_E_INVALID
+    assert _fwd(_shape(dtype=7), cc) == BSX_E_INVALID
+    assert _fwd(_shape(block_size=0), cc) == BSX_E_INVALID
+    assert _fwd(_shape(n_blocks=-1), cc) == BSX_E_INVALID
+    assert _fwd(_shape(ctx_len=-5), cc) == BSX_E_INVALID
+    k2, bad_range = _chunks([0, 600], [512, 512])        # runs past S
+    assert _fwd(_shape(), bad_range) == BSX_E_INVALID
+    k3, neg = _chunks([0, 512], [512, -1])
+    assert _fwd(_shape(), neg) == BSX_E_INVALID
+    k4, bad_slot = _chunks([0, 512], [512, 512], slot=[0, 2], n_slots=2)
+    assert _fwd(_shape(), bad_slot) == BSX_E_INVALID
+    k5, no_slot = _chunks([0, 512], [512, 512], None, n_slots=1)
+    assert _fwd(_shape(), no_slot) == BSX_E_INVALID
+    # self keys: both or neither
+    assert lib().bsx_attn_fwd(ctypes.byref(_shape()), 1, 1, 1, 1, None, 1, 1, ctypes.byref(cc),
+                              1, 1, 1, 1 << 20, None) == BSX_E_INVALID
+    # workspace too small
+    need = lib().bsx_fwd_workspace(ctypes.byref(_shape()), ctypes.byref(cc))
+    assert need > 0
+    assert _fwd(_shape(), cc, ws_bytes=need - 1) == BSX_E_WORKSPACE
+    assert b"workspace" in lib().bsx_last_error()
+
+
+def test_merge_and_cost_reject_bad_arguments():
+    L = lib()
+    assert L.bsx_lse_merge(0, 10, 128, 1, 1, 1, 1, None) == BSX_E_INVALID
+    assert L.bsx_lse_merge(2, 10, 130, 1, 1, 1, 1, None) == BSX_E_INVALID
+    assert L.bsx_lse_merge(2, -1, 128, 1, 1, 1, 1, None) == BSX_E_INVALID
+    assert L.bsx_lse_merge(2, 10, 128, None, 1, 1, 1, None) == BSX_E_INVALID
+    keep, cc = _chunks([0], [1024])
+    sh = _shape()
+    assert L.bsx_cost(ctypes.byref(sh), 1, 1, ctypes.byref(cc), 1, 1, None, 1, 1 << 20,
+                      None) == BSX_E_INVALID
+    assert L.bsx_cost(ctypes.byref(sh), 1, 1, ctypes.byref(cc), 1, 1, 1, 1, 8,
+                      None) == BSX_E_WORKSPACE
+    keep2, bad = _chunks([1000], [100])
+    assert L.bsx_cost(ctypes.byref(sh), 1, 1, ctypes.byref(bad), 1, 1, 1, 1, 1 << 20,
+                      None) == BSX_E_INVALID
+
+
+def test_backward_rejects_f32_and_missing_self_grads():
+    L = lib()
+    keep, cc = _chunks([0], [1024])
+    f = 1
+    assert L.bsx_attn_bwd(ctypes.byref(_shape(dtype=0)), f, f, f, f, f, f, f, f, f, f,
+                          ctypes.byref(cc), f, f, f, f, f, f, 1 << 20, None) == BSX_E_UNSUPPORTED
+    assert L.bsx_attn_bwd(ctypes.byref(_shape()), f, f, f, f, f, f, f, f, f, f,
+                          ctypes.byref(cc), f, f, f, None, f, f, 1 << 20, None) == BSX_E_INVALID
+
+
+def test_python_binding_checks_buffer_shapes_on_cpu_tensors():
+    import torch
+    shape = bsx.Shape(n_blocks=1, block_size=16, n_q_heads=8, n_kv_heads=2, ctx_len=64)
+    ch = bsx.Chunks([0], [64])
+    q = torch.zeros((16, 8, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bsx.attn_fwd(shape, q, q, q, None, None, None, None, ch)

@@ -1,0 +1,333 @@
+"""GPU parity: libbsx (through its C ABI) against the fp64 oracle on seeded inputs.
+
+Integers (visible-key counts, chunk costs, LPT plans) must match bit for bit.  Floating
+point: max abs error <= 1e-5 on O and LSE for f32 inputs; <= 2e-2 on O and <= 2e-3 on LSE
+for bf16 inputs with f32 accumulation.  Rows with no visible key must be LSE = -inf on both
+sides.  Small workloads are compared in full; full-size workloads on sampled (block, KV head)
+pairs, computed by the oracle one pair at a time, in the launch configuration the benchmark
+times.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_cross_amd as bsx
+import oracle
+from block_sparse_cross_amd.pipeline import make_plan
+from parity_helpers import (compare_partials, log, oracle_plan, sample_pairs, shape_of,
+                            tolerances, upload)
+from workloads import CONFIGS, make_workload
+from workloads.gen import custom_workload, draw_merge_sets
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------- cost + LPT
+
+@pytest.mark.parametrize("idx", range(5))
+def test_cost_kernel_bit_exact(idx):
+    wl = make_workload(CONFIGS[idx])
+    log(f"cost kernel, workload {wl.cfg.name}: blocks={wl.n_blocks} chunks={wl.n_chunks}")
+    shape = shape_of(wl)
+    anchor = torch.from_numpy(wl.anchor).cuda()
+    begin = torch.from_numpy(wl.ctx_begin).cuda()
+    counts, cost, err = bsx.cost(shape, anchor, begin, bsx.Chunks(wl.chunk_start, wl.chunk_len))
+    counts2, cost2, _ = bsx.cost(shape, anchor, begin, bsx.Chunks(wl.chunk_start, wl.chunk_len))
+    ref_counts, ref_cost = oracle.chunk_costs(wl.anchor, wl.ctx_begin, wl.cfg.block_size,
+                                              wl.chunk_start, wl.chunk_len)
+    assert np.array_equal(counts.cpu().numpy(), ref_counts)
+    assert np.array_equal(cost.cpu().numpy(), ref_cost)
+    assert int(err.item()) == 0
+    assert torch.equal(counts, counts2) and torch.equal(cost, cost2)
+
+
+def test_cost_kernel_ragged_chunks_and_bad_mask():
+    rng = np.random.default_rng(17)
+    S = 5000
+    cuts = np.sort(rng.integers(0, S + 1, size=37))
+    bounds = np.concatenate([[0], cuts, [S]])
+    starts, lens = bounds[:-1], np.diff(bounds)
+    hi = rng.integers(0, S + 1, size=300)
+    lo = np.minimum(hi, rng.integers(0, S + 1, size=300))
+    shape = bsx.Shape(n_blocks=300, block_size=7, n_q_heads=4, n_kv_heads=2, ctx_len=S)
+    counts, cost, err = bsx.cost(shape, torch.from_numpy(hi).cuda(), torch.from_numpy(lo).cuda(),
+                                 bsx.Chunks(starts, lens))
+    rc, rcost = oracle.chunk_costs(hi, lo, 7, starts, lens)
+    assert np.array_equal(counts.cpu().numpy(), rc) and np.array_equal(cost.cpu().numpy(), rcost)
+    assert int(err.item()) == 0
+    bad_hi = hi.copy()
+    bad_hi[5] = S + 3
+    _, _, err = bsx.cost(shape, torch.from_numpy(bad_hi).cuda(), torch.from_numpy(lo).cuda(),
+                         bsx.Chunks(starts, lens))
+    assert int(err.item()) == 1
+    bad_lo = lo.copy()
+    bad_lo[7] = hi[7] + 1
+    _, _, err = bsx.cost(shape, torch.from_numpy(hi).cuda(), torch.from_numpy(bad_lo).cuda(),
+                         bsx.Chunks(starts, lens))
+    assert int(err.item()) == 1
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_plan_matches_oracle(idx):
+    wl = make_workload(CONFIGS[idx])
+    c = wl.cfg
+    ref = oracle_plan(wl)
+    plan = make_plan(shape_of(wl), wl.chunk_start, wl.chunk_len, c.slot_mode, c.n_bins,
+                     torch.from_numpy(wl.anchor).cuda(), torch.from_numpy(wl.ctx_begin).cuda())
+    assert np.array_equal(plan.chunk_cost, ref["cost"])
+    assert np.array_equal(plan.bin_of, ref["bin_of"])
+    assert plan.makespan == ref["makespan"]
+    assert plan.imbalance == pytest.approx(ref["imbalance"], abs=1e-15)
+    assert np.array_equal(plan.local_chunks, ref["local"])
+    log(f"  {c.name}: LPT imbalance {plan.imbalance * 100:.3f}% over {c.n_bins} bins")
+
+
+# ----------------------------------------------------------------------------- forward
+
+def _run_forward(wl, plan_ref):
+    k_loc, v_loc = wl.kv_chunks(plan_ref["local"])
+    dev = upload(wl, k_loc, v_loc)
+    shape = shape_of(wl)
+    starts = wl.chunk_start[plan_ref["local"]]
+    lens = wl.chunk_len[plan_ref["local"]]
+    chunks = bsx.Chunks(starts, lens, plan_ref["slot_of"], plan_ref["n_slots"])
+    with_self = wl.cfg.self_slot
+    o, lse = bsx.attn_fwd(shape, dev["q"], dev["k"], dev["v"],
+                          dev["k_self"] if with_self else None,
+                          dev["v_self"] if with_self else None,
+                          dev["anchor"], dev["ctx_begin"], chunks)
+    return dev, k_loc, v_loc, starts, lens, o, lse
+
+
+def _oracle_partials(wl, k_loc, v_loc, starts, lens, slot_of, n_slots, with_self, pairs=None):
+    if pairs is None:
+        return oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                    wl.ctx_begin, wl.cfg.block_size, starts, lens, slot_of,
+                                    n_slots, with_self=with_self)
+    ns = n_slots + (1 if with_self else 0)
+    nq, hq, d = wl.q.shape
+    o = np.full((ns, nq, hq, d), np.nan)
+    lse = np.full((ns, nq, hq), np.nan)
+    for b, g in pairs:
+        po, pl = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                      wl.ctx_begin, wl.cfg.block_size, starts, lens, slot_of,
+                                      n_slots, with_self=with_self, blocks=[b], groups=[g])
+        sel = ~np.isnan(pl)
+        o[sel] = po[sel]
+        lse[sel] = pl[sel]
+    return o, lse
+
+
+def test_forward_f32_tiny_full():
+    wl = make_workload(CONFIGS[0])
+    log(f"forward f32, {wl.cfg.name}")
+    ref = oracle_plan(wl)
+    dev, k_loc, v_loc, starts, lens, o, lse = _run_forward(wl, ref)
+    ro, rl = _oracle_partials(wl, k_loc, v_loc, starts, lens, ref["slot_of"], ref["n_slots"], True)
+    tol_o, tol_l = tolerances("f32")
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_o, tol_l, "partials")
+    mo, ml = bsx.lse_merge(o, lse)
+    uo, ul = oracle.attention(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor, wl.ctx_begin,
+                              wl.cfg.block_size)
+    compare_partials(mo.cpu().numpy(), ml.cpu().numpy(), uo, ul, tol_o, tol_l, "merged")
+
+
+def test_forward_bf16_a3b_full():
+    wl = make_workload(CONFIGS[1])
+    log(f"forward bf16, {wl.cfg.name} (all rows)")
+    ref = oracle_plan(wl)
+    dev, k_loc, v_loc, starts, lens, o, lse = _run_forward(wl, ref)
+    o2, lse2 = bsx.attn_fwd(shape_of(wl), dev["q"], dev["k"], dev["v"], dev["k_self"],
+                            dev["v_self"], dev["anchor"], dev["ctx_begin"],
+                            bsx.Chunks(starts, lens, ref["slot_of"], ref["n_slots"]))
+    assert torch.equal(lse, lse2)  # deterministic: no atomics, fixed order
+    ro, rl = _oracle_partials(wl, k_loc, v_loc, starts, lens, ref["slot_of"], ref["n_slots"], True)
+    tol_o, tol_l = tolerances("bf16")
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_o, tol_l, "partials")
+    mo, ml = bsx.lse_merge(o, lse)
+    uo, ul = oracle.attention(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor, wl.ctx_begin,
+                              wl.cfg.block_size)
+    compare_partials(mo.cpu().numpy(), ml.cpu().numpy(), uo, ul, tol_o, tol_l, "merged")
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_forward_bf16_full_size_sampled(idx):
+    wl = make_workload(CONFIGS[idx])
+    log(f"forward bf16, {wl.cfg.name} (sampled block/head pairs)")
+    ref = oracle_plan(wl)
+    dev, k_loc, v_loc, starts, lens, o, lse = _run_forward(wl, ref)
+    pairs = sample_pairs(wl, 6, seed=idx)
+    ro, rl = _oracle_partials(wl, k_loc, v_loc, starts, lens, ref["slot_of"], ref["n_slots"],
+                              wl.cfg.self_slot, pairs)
+    tol_o, tol_l = tolerances("bf16")
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_o, tol_l, "partials")
+    if wl.cfg.slot_mode == "rank":
+        return
+    mo, ml = bsx.lse_merge(o, lse)
+    uo = np.full(wl.q.shape, np.nan)
+    ul = np.full(wl.q.shape[:2], np.nan)
+    grp = wl.cfg.group
+    B = wl.cfg.block_size
+    for b, g in pairs:
+        bo, bl = oracle.attention_block(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                        wl.ctx_begin, B, b, g)
+        uo[b * B:(b + 1) * B, g * grp:(g + 1) * grp] = bo
+        ul[b * B:(b + 1) * B, g * grp:(g + 1) * grp] = bl
+    compare_partials(mo.cpu().numpy(), ml.cpu().numpy(), uo, ul, tol_o, tol_l, "merged")
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+EDGE_CASES = {
+    # name: (ctx_len, H_q, H_kv, B, anchors, begins, chunk starts, chunk lens, slot_of, n_slots)
+    "ragged_chunks": (3000, 8, 2, 16, [0, 1, 777, 2999, 3000], None,
+                      [0, 1000, 1999, 2000], [1000, 999, 1, 1000], None, None),
+    "anchor_zero_and_gqa8": (2048, 32, 4, 16, [0, 0, 64, 2048], None,
+                             [0, 1024], [1024, 1024], None, None),
+    "mha_block5": (700, 4, 4, 5, [3, 100, 650, 699, 700, 0, 350], None,
+                   [0, 350], [350, 350], None, None),
+    "gqa2_block8": (900, 8, 4, 8, [899, 450, 10], None, [0, 300, 600], [300, 300, 300],
+                    [1, 0, 1], 2),
+    "packed_samples": (4096, 16, 2, 16, [100, 1500, 1600, 4000, 2500], [0, 0, 1000, 2400, 2400],
+                       list(range(0, 4096, 512)), [512] * 8, [0, 1, 2, 0, 1, 2, 0, 1], 3),
+    "one_chunk": (1536, 8, 1, 16, [1536, 700], None, [0], [1536], None, None),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", sorted(EDGE_CASES))
+def test_forward_edge_cases(case, dtype):
+    S, hq, hk, B, an, be, cs, cl, slot_of, n_slots = EDGE_CASES[case]
+    log(f"edge case {case} ({dtype})")
+    be = [0] * len(an) if be is None else be
+    wl = custom_workload(seed=zlib.crc32(case.encode()) % 1000, ctx_len=S, n_q_heads=hq, n_kv_heads=hk,
+                         dtype=dtype, sigma=1.0 if dtype == "f32" else 0.5, block_size=B,
+                         anchor=an, ctx_begin=be, chunk_start=cs, chunk_len=cl)
+    n = len(cs)
+    slot_of = np.arange(n) if slot_of is None else np.asarray(slot_of)
+    n_slots = n if n_slots is None else n_slots
+    k_loc, v_loc = wl.kv_chunks()
+    dev = upload(wl, k_loc, v_loc)
+    chunks = bsx.Chunks(cs, cl, slot_of, n_slots)
+    o, lse = bsx.attn_fwd(shape_of(wl), dev["q"], dev["k"], dev["v"], dev["k_self"],
+                          dev["v_self"], dev["anchor"], dev["ctx_begin"], chunks)
+    ro, rl = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, B, np.asarray(cs), np.asarray(cl), slot_of, n_slots)
+    tol_o, tol_l = tolerances(dtype)
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_o, tol_l, "partials")
+    mo, ml = bsx.lse_merge(o, lse)
+    pos = np.concatenate([np.arange(s, s + c) for s, c in zip(cs, cl)])
+    k_glob = np.zeros((S, hk, 128), np.float32)
+    v_glob = np.zeros((S, hk, 128), np.float32)
+    k_glob[pos], v_glob[pos] = k_loc, v_loc
+    uo, ul = oracle.attention(wl.q, k_glob, v_glob, wl.k_self, wl.v_self, wl.anchor,
+                              wl.ctx_begin, B)
+    compare_partials(mo.cpu().numpy(), ml.cpu().numpy(), uo, ul, tol_o, tol_l, "merged")
+
+
+def test_forward_rank_share_without_self_and_empty_rows():
+    """A non-contiguous rank chunk list fused into one slot, no self keys; blocks whose range
+    misses every local chunk must come out as LSE = -inf."""
+    wl = custom_workload(seed=5, ctx_len=8192, n_q_heads=32, n_kv_heads=4, block_size=16,
+                         anchor=[0, 10, 1000, 3000, 5000, 8192], ctx_begin=[0] * 6,
+                         chunk_start=[4096, 1024, 7168], chunk_len=[1024, 1024, 1024])
+    k_loc, v_loc = wl.kv_chunks()
+    dev = upload(wl, k_loc, v_loc)
+    chunks = bsx.Chunks(wl.chunk_start, wl.chunk_len, [0, 0, 0], 1)
+    o, lse = bsx.attn_fwd(shape_of(wl), dev["q"], dev["k"], dev["v"], None, None, dev["anchor"],
+                          dev["ctx_begin"], chunks)
+    ro, rl = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, 16, wl.chunk_start, wl.chunk_len, [0, 0, 0], 1,
+                                  with_self=False)
+    assert np.isneginf(rl[0, :32]).all()  # blocks 0, 1 see none of the local chunks
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, 2e-2, 2e-3, "rank partial")
+
+
+def test_forward_sharp_scores():
+    """The a3b shape with Q scaled by 4 (exact in bf16): score spread ~4x, so the online
+    softmax rescaling is exercised far from the near-uniform regime."""
+    wl = make_workload(CONFIGS[1])
+    wl.q = wl.q * 4.0
+    ref = oracle_plan(wl)
+    dev, k_loc, v_loc, starts, lens, o, lse = _run_forward(wl, ref)
+    pairs = sample_pairs(wl, 8, seed=99)
+    ro, rl = _oracle_partials(wl, k_loc, v_loc, starts, lens, ref["slot_of"], ref["n_slots"],
+                              True, pairs)
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, 2e-2, 2e-3, "sharp partials")
+
+
+def test_forward_custom_scale():
+    wl = custom_workload(seed=8, ctx_len=1000, n_q_heads=8, n_kv_heads=2, block_size=16,
+                         anchor=[500, 1000], ctx_begin=[0, 0], chunk_start=[0, 500],
+                         chunk_len=[500, 500])
+    k_loc, v_loc = wl.kv_chunks()
+    dev = upload(wl, k_loc, v_loc)
+    shape = shape_of(wl)
+    shape.scale = 0.3
+    o, lse = bsx.attn_fwd(shape, dev["q"], dev["k"], dev["v"], dev["k_self"], dev["v_self"],
+                          dev["anchor"], dev["ctx_begin"], bsx.Chunks(wl.chunk_start, wl.chunk_len))
+    ro, rl = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, 16, wl.chunk_start, wl.chunk_len, [0, 1], 2,
+                                  scale=0.3)
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, 2e-2, 2e-3, "scale 0.3")
+
+
+# ----------------------------------------------------------------------------- merge
+
+def test_merge_rank_sets_full_size_sampled():
+    """64 seeded partial sets of [2048, 32, 128] (one rank's view at CP size 64)."""
+    cfg = CONFIGS[3]
+    n_rows = 2048 * 32
+    log("merge, 64 seeded sets of [2048, 32, 128]")
+    o_sets, l_sets = draw_merge_sets(cfg, cfg.n_merge_sets, n_rows, 128)
+    o_t = torch.from_numpy(o_sets).cuda()
+    l_t = torch.from_numpy(l_sets).cuda()
+    mo, ml = bsx.lse_merge(o_t, l_t)
+    rows = np.random.default_rng(3).choice(n_rows, size=512, replace=False)
+    rows = np.concatenate([rows, [0, n_rows - 1]])
+    ro, rl = oracle.lse_merge(o_sets[:, rows], l_sets[:, rows])
+    got_o = mo.cpu().numpy()[rows]
+    got_l = ml.cpu().numpy()[rows]
+    np.testing.assert_allclose(got_l, rl, atol=1e-5, rtol=0)
+    np.testing.assert_allclose(got_o, ro, atol=1e-5, rtol=0)
+
+
+def test_merge_with_empty_partials():
+    rng = np.random.default_rng(4)
+    P, R, d = 7, 1000, 128
+    o = rng.standard_normal((P, R, d)).astype(np.float32)
+    lse = (rng.standard_normal((P, R)) * 5).astype(np.float32)
+    drop = rng.random((P, R)) < 0.4
+    lse[drop] = -np.inf
+    o[drop] = np.nan  # unspecified O of an empty partial must never be read
+    lse[:, 10] = -np.inf  # a row with no visible key at all
+    mo, ml = bsx.lse_merge(torch.from_numpy(o).cuda(), torch.from_numpy(lse).cuda())
+    ro, rl = oracle.lse_merge(o, lse)
+    got_o, got_l = mo.cpu().numpy(), ml.cpu().numpy()
+    assert np.isneginf(got_l[10]) and np.all(got_o[10] == 0)
+    np.testing.assert_array_equal(np.isneginf(got_l), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    np.testing.assert_allclose(got_l[fin], rl[fin], atol=1e-5, rtol=0)
+    np.testing.assert_allclose(got_o[fin], ro[fin], atol=1e-5, rtol=0)
+
+
+@pytest.mark.parametrize("P,R,d", [(1, 5, 128), (3, 130, 64), (13, 77, 4), (2, 64, 512)])
+def test_merge_shapes(P, R, d):
+    rng = np.random.default_rng(P * 1000 + R)
+    o = rng.standard_normal((P, R, d)).astype(np.float32)
+    lse = rng.standard_normal((P, R)).astype(np.float32)
+    mo, ml = bsx.lse_merge(torch.from_numpy(o).cuda(), torch.from_numpy(lse).cuda())
+    ro, rl = oracle.lse_merge(o, lse)
+    np.testing.assert_allclose(ml.cpu().numpy(), rl, atol=1e-5, rtol=0)
+    np.testing.assert_allclose(mo.cpu().numpy(), ro, atol=1e-5, rtol=0)
