@@ -1,0 +1,322 @@
+"""Benchmark of the draft-query block-sparse cross-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole hot path over one batch of synthetic inputs that
+are already resident in HBM: the per-chunk cost kernel, the LPT plan (host, after
+the one readback of chunk costs) for planned workloads, the forward partials, the
+exact LSE merge, and for the training workload the backward pass.  The default
+workload is the Qwen3.5-35B-A3B-drafter shape (S = 16384, H_q = 32, H_kv = 4,
+d = 128, 32 anchors x 16 draft queries, 16 KV chunks of 1024 with one partial per
+chunk plus the draft block's own keys).
+
+Prints one JSON line: useful TFLOP/s (masked-out and padded work excluded) of the
+step, a roofline object for the dominant kernel (the forward attention, timed with
+HIP events on the stream it runs on), and the fp64 oracle timed on host cores on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "useful TFLOP/s of block-sparse cross-attn fwd (+bwd) and % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="a3b_s16k")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the oracle's CPU baseline sample (0 skips it)")
+    ap.add_argument("--fwd-reps", type=int, default=50,
+                    help="event-timed launches of the forward kernel for the roofline")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a reference "
+                         "dispatch for scaling HBM byte counters)")
+    return ap.parse_args()
+
+
+def useful_fwd_flops(wl, with_self: bool) -> float:
+    c = wl.cfg
+    vis = float((wl.anchor - wl.ctx_begin).sum()) * c.block_size
+    if with_self:
+        vis += wl.n_blocks * c.block_size * c.block_size
+    return 4.0 * c.head_dim * c.n_q_heads * vis
+
+
+def rank_fwd_flops(wl, local_chunks) -> float:
+    """Useful flops of one rank's share: visible (query, key) pairs in its local chunks."""
+    c = wl.cfg
+    tot = 0.0
+    for ch in local_chunks:
+        c0 = int(wl.chunk_start[ch])
+        c1 = c0 + int(wl.chunk_len[ch])
+        ov = np.clip(np.minimum(wl.anchor, c1) - np.maximum(wl.ctx_begin, c0), 0, None)
+        tot += float(ov.sum()) * c.block_size
+    return 4.0 * c.head_dim * c.n_q_heads * tot
+
+
+class Step:
+    """Device-resident inputs, preallocated outputs and workspaces, and one-step runner."""
+
+    def __init__(self, wl, device):
+        import torch
+
+        import block_sparse_cross_amd as bsx
+        from block_sparse_cross_amd.pipeline import make_plan
+
+        self.torch, self.bsx, self.make_plan = torch, bsx, make_plan
+        self.wl, self.cfg, self.dev = wl, wl.cfg, device
+        c = wl.cfg
+        self.shape = bsx.Shape(n_blocks=wl.n_blocks, block_size=c.block_size,
+                               n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads, ctx_len=c.ctx_len,
+                               head_dim=c.head_dim, dtype=c.dtype)
+        dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+        up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(device)  # noqa: E731
+        self.anchor = torch.from_numpy(wl.anchor).to(device)
+        self.begin = torch.from_numpy(wl.ctx_begin).to(device)
+        self.all_chunks = bsx.Chunks(wl.chunk_start, wl.chunk_len)
+        self.cost_ws = torch.empty(bsx.cost_workspace_bytes(wl.n_chunks), dtype=torch.uint8,
+                                   device=device)
+        self.cost_out = (None, torch.empty(wl.n_chunks, dtype=torch.int64, device=device),
+                         torch.empty(1, dtype=torch.int32, device=device))
+        # plan once to learn which chunks are local (deterministic: every step replans the same)
+        self.plan0 = make_plan(self.shape, wl.chunk_start, wl.chunk_len, c.slot_mode, c.n_bins,
+                               self.anchor, self.begin, self.cost_ws, self.cost_out)
+        k, v = wl.kv_chunks(self.plan0.local_chunks)
+        self.q, self.k, self.v = up(wl.q), up(k), up(v)
+        self.ks = up(wl.k_self) if c.self_slot else None
+        self.vs = up(wl.v_self) if c.self_slot else None
+        ch = self.plan0.chunks
+        n_out = ch.n_slots + (1 if c.self_slot else 0)
+        nq = wl.n_queries
+        self.o_part = torch.empty((n_out, nq, c.n_q_heads, c.head_dim), dtype=torch.float32,
+                                  device=device)
+        self.lse_part = torch.empty((n_out, nq, c.n_q_heads), dtype=torch.float32, device=device)
+        self.fwd_ws = torch.empty(max(bsx.fwd_workspace_bytes(self.shape, ch), 256),
+                                  dtype=torch.uint8, device=device)
+        self.o = torch.empty((nq, c.n_q_heads, c.head_dim), dtype=torch.float32, device=device)
+        self.lse = torch.empty((nq, c.n_q_heads), dtype=torch.float32, device=device)
+        self.backward = c.backward
+        if self.backward:
+            self.d_o = up(wl.d_o)
+            nl = ch.n_local
+            f32 = torch.float32
+            self.grads = (torch.empty((nq, c.n_q_heads, c.head_dim), dtype=f32, device=device),
+                          torch.empty((nl, c.n_kv_heads, c.head_dim), dtype=f32, device=device),
+                          torch.empty((nl, c.n_kv_heads, c.head_dim), dtype=f32, device=device),
+                          torch.empty((nq, c.n_kv_heads, c.head_dim), dtype=f32, device=device),
+                          torch.empty((nq, c.n_kv_heads, c.head_dim), dtype=f32, device=device))
+            self.bwd_ws = torch.empty(max(bsx.bwd_workspace_bytes(self.shape, ch), 256),
+                                      dtype=torch.uint8, device=device)
+        if c.slot_mode == "rank":
+            self.fwd_flops = rank_fwd_flops(wl, self.plan0.local_chunks)
+        else:
+            self.fwd_flops = useful_fwd_flops(wl, c.self_slot)
+        self.step_flops = self.fwd_flops * (3.5 if self.backward else 1.0)
+
+    def prepare(self):
+        """Validated, marshalled calls for the per-step launches (low host overhead)."""
+        bsx = self.bsx
+        self.cost_call = bsx.prepare_cost(self.shape, self.anchor, self.begin, self.all_chunks,
+                                          self.cost_out[1], self.cost_out[2], ws=self.cost_ws)
+        self.fwd_call = bsx.prepare_attn_fwd(self.shape, self.q, self.k, self.v, self.ks, self.vs,
+                                             self.anchor, self.begin, self.plan0.chunks,
+                                             self.o_part, self.lse_part, self.fwd_ws)
+        self.merge_call = bsx.prepare_lse_merge(self.o_part, self.lse_part, self.o, self.lse)
+        self.bwd_call = None
+        if self.backward:
+            self.bwd_call = bsx.prepare_attn_bwd(self.shape, self.q, self.k, self.v, self.ks,
+                                                 self.vs, self.o, self.lse, self.d_o, self.anchor,
+                                                 self.begin, self.plan0.chunks, self.grads,
+                                                 self.bwd_ws)
+
+    def plan(self):
+        """Cost kernel, then (planned workloads) readback of chunk costs and LPT."""
+        c = self.cfg
+        self.cost_call()
+        if c.slot_mode == "per_chunk":
+            return  # one partial per chunk: the plan does not depend on the costs
+        cost_host = self.cost_out[1].cpu().numpy()
+        r = self.bsx.lpt(cost_host, c.n_bins)
+        wl = self.wl
+        if c.slot_mode == "lpt":
+            chunks = self.bsx.Chunks(wl.chunk_start, wl.chunk_len, r.bin_of, c.n_bins)
+        else:
+            rank = int(np.argmax(r.loads))
+            mine = np.nonzero(r.bin_of == rank)[0]
+            if not np.array_equal(mine, self.plan0.local_chunks):
+                raise RuntimeError("plan changed between steps")
+            chunks = self.bsx.Chunks(wl.chunk_start[mine], wl.chunk_len[mine],
+                                     np.zeros(len(mine), np.int32), 1)
+        self.fwd_call.set_chunks(chunks, self.plan0.chunks)
+        if self.bwd_call is not None:
+            self.bwd_call.set_chunks(chunks, self.plan0.chunks)
+
+    def forward(self, chunks=None):
+        self.fwd_call()
+
+    def merge(self):
+        self.merge_call()
+
+    def run(self):
+        self.plan()
+        self.fwd_call()
+        self.merge_call()
+        if self.bwd_call is not None:
+            self.bwd_call()
+
+
+def time_forward(step: Step, reps: int):
+    """Average duration of one forward launch, from HIP events on the launch stream."""
+    torch = step.torch
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        step.forward()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        step.forward()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps * 1e-3
+
+
+def cpu_baseline(wl, plan0, seconds: float):
+    """The fp64 oracle (forward partials of every slot + merge) on (block, KV head) pairs taken
+    in a fixed seeded order until the time budget is spent; useful TFLOP/s of that sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    c = wl.cfg
+    k, v = wl.kv_chunks(plan0.local_chunks)
+    ch = plan0.chunks
+    slot_of = np.arange(ch.n_chunks) if ch.slot is None else ch.slot
+    rng = np.random.default_rng(0)
+    pairs = [(b, g) for b in range(wl.n_blocks) for g in range(c.n_kv_heads)]
+    order = rng.permutation(len(pairs))
+    grp = c.group
+    done_flops, n_done = 0.0, 0
+    t0 = time.perf_counter()
+    for idx in order:
+        b, g = pairs[idx]
+        o, lse = oracle.slot_partials(wl.q, k, v, wl.k_self, wl.v_self, wl.anchor, wl.ctx_begin,
+                                      c.block_size, ch.start, ch.length, slot_of, ch.n_slots,
+                                      with_self=c.self_slot, blocks=[b], groups=[g])
+        sl = (slice(None), slice(b * c.block_size, (b + 1) * c.block_size),
+              slice(g * grp, (g + 1) * grp))
+        oracle.lse_merge(o[sl].reshape(o.shape[0], -1, o.shape[-1]),
+                         lse[sl].reshape(lse.shape[0], -1))
+        vis = 0
+        for s0, n in zip(ch.start, ch.length):
+            vis += max(0, min(int(wl.anchor[b]), s0 + n) - max(int(wl.ctx_begin[b]), s0))
+        if c.self_slot:
+            vis += c.block_size
+        done_flops += 4.0 * c.head_dim * grp * c.block_size * vis
+        n_done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"fp64 oracle forward partials of all {ch.n_slots + int(c.self_slot)} slots "
+                      f"+ merge for {n_done} of {len(pairs)} (block, KV head) pairs of the same "
+                      f"workload, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU Split-KV exchange is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from workloads import get_config, make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 18  # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    cfg = get_config(args.workload)
+    wl = make_workload(cfg, args.seed)
+    step = Step(wl, dev)
+    step.prepare()
+    print(f"# workload {cfg.name}: blocks={wl.n_blocks} queries={wl.n_queries} "
+          f"local_chunks={len(step.plan0.local_chunks)} fwd useful GFLOP={step.fwd_flops / 1e9:.2f}",
+          file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt / args.steps * 1e3
+    value = step.step_flops / (dt / args.steps) / 1e12
+
+    fwd_s = time_forward(step, args.fwd_reps)
+    achieved = step.fwd_flops / fwd_s / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "kernel": "fwd_bf16_kernel",
+                "launch_us": round(fwd_s * 1e6, 2),
+                "flops_per_launch": step.fwd_flops}
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(wl, step.plan0, args.cpu_seconds)
+
+    c = cfg
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": c.name, "ctx_len": c.ctx_len, "n_q_heads": c.n_q_heads,
+                   "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim,
+                   "n_anchors": wl.n_blocks, "block_size": c.block_size,
+                   "n_queries": wl.n_queries, "chunk_len": c.chunk_len,
+                   "n_chunks": wl.n_chunks, "slot_mode": c.slot_mode, "n_bins": c.n_bins,
+                   "backward": c.backward, "seed": wl.cfg.seed},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if c.slot_mode != "per_chunk":
+        line["lpt_imbalance"] = step.plan0.imbalance
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

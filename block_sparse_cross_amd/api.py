@@ -148,7 +148,8 @@ def cost_workspace_bytes(n_chunks: int) -> int:
 
 
 def cost(shape: Shape, anchor: torch.Tensor, ctx_begin: torch.Tensor, chunks: Chunks,
-         with_counts: bool = True, ws: Optional[torch.Tensor] = None, out=None):
+         with_counts: bool = True, ws: Optional[torch.Tensor] = None, out=None,
+         _launch: bool = True):
     """-> (counts [n_blocks, n_chunks] int64 or None, chunk_cost [n_chunks] int64, mask_err int32[1])."""
     dev = anchor.device
     _need(anchor, "anchor", (shape.n_blocks,), torch.int64, dev)
@@ -167,6 +168,8 @@ def cost(shape: Shape, anchor: torch.Tensor, ctx_begin: torch.Tensor, chunks: Ch
         _need(mask_err, "mask_err", (1,), torch.int32, dev)
     nbytes = cost_workspace_bytes(nc)
     ws = _workspace(nbytes, dev, ws)
+    if not _launch:
+        return counts, chunk_cost, mask_err
     sc, cc = shape.c(), chunks.c()
     check(lib().bsx_cost(ctypes.byref(sc), _ptr(anchor), _ptr(ctx_begin), ctypes.byref(cc),
                          _ptr(counts), _ptr(chunk_cost), _ptr(mask_err), _ptr(ws),
@@ -180,7 +183,8 @@ def fwd_workspace_bytes(shape: Shape, chunks: Chunks) -> int:
 
 
 def attn_fwd(shape: Shape, q, k, v, k_self, v_self, anchor, ctx_begin, chunks: Chunks,
-             o_part=None, lse_part=None, ws: Optional[torch.Tensor] = None):
+             o_part=None, lse_part=None, ws: Optional[torch.Tensor] = None,
+             _launch: bool = True):
     """-> (o_part [n_out, N_q, H_q, d] f32, lse_part [n_out, N_q, H_q] f32)."""
     dev = q.device
     dt = shape.torch_dtype
@@ -204,6 +208,8 @@ def attn_fwd(shape: Shape, q, k, v, k_self, v_self, anchor, ctx_begin, chunks: C
     _need(o_part, "o_part", (n_out, nq, hq, d), torch.float32, dev)
     _need(lse_part, "lse_part", (n_out, nq, hq), torch.float32, dev)
     ws = _workspace(fwd_workspace_bytes(shape, chunks), dev, ws)
+    if not _launch:
+        return o_part, lse_part
     sc, cc = shape.c(), chunks.c()
     check(lib().bsx_attn_fwd(ctypes.byref(sc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_self),
                              _ptr(v_self), _ptr(anchor), _ptr(ctx_begin), ctypes.byref(cc),
@@ -211,7 +217,8 @@ def attn_fwd(shape: Shape, q, k, v, k_self, v_self, anchor, ctx_begin, chunks: C
     return o_part, lse_part
 
 
-def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, o_out=None, lse_out=None):
+def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, o_out=None, lse_out=None,
+              _launch: bool = True):
     """o_parts [P, *rows, d], lse_parts [P, *rows] (f32) -> (o [*rows, d], lse [*rows])."""
     dev = o_parts.device
     P = int(o_parts.shape[0])
@@ -226,6 +233,8 @@ def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, o_out=None, lse_ou
         lse_out = torch.empty(rows_shape, dtype=torch.float32, device=dev)
     _need(o_out, "o_out", (*rows_shape, d), torch.float32, dev)
     _need(lse_out, "lse_out", rows_shape, torch.float32, dev)
+    if not _launch:
+        return o_out, lse_out
     check(lib().bsx_lse_merge(P, n_rows, d, _ptr(o_parts), _ptr(lse_parts), _ptr(o_out),
                               _ptr(lse_out), _stream(o_parts)))
     return o_out, lse_out
@@ -237,7 +246,8 @@ def bwd_workspace_bytes(shape: Shape, chunks: Chunks) -> int:
 
 
 def attn_bwd(shape: Shape, q, k, v, k_self, v_self, o, lse, d_o, anchor, ctx_begin,
-             chunks: Chunks, out=None, ws: Optional[torch.Tensor] = None):
+             chunks: Chunks, out=None, ws: Optional[torch.Tensor] = None,
+             _launch: bool = True):
     """-> (dq, dk, dv, dk_self, dv_self), all f32 (dk_self/dv_self None without self keys)."""
     dev = q.device
     dt = shape.torch_dtype
@@ -272,6 +282,8 @@ def attn_bwd(shape: Shape, q, k, v, k_self, v_self, o, lse, d_o, anchor, ctx_beg
         _need(dks, "dk_self", (nq, hk, d), f32, dev)
         _need(dvs, "dv_self", (nq, hk, d), f32, dev)
     ws = _workspace(bwd_workspace_bytes(shape, chunks), dev, ws)
+    if not _launch:
+        return dq, dk, dv, dks, dvs
     sc, cc = shape.c(), chunks.c()
     check(lib().bsx_attn_bwd(ctypes.byref(sc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_self),
                              _ptr(v_self), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(anchor),
@@ -280,6 +292,96 @@ def attn_bwd(shape: Shape, q, k, v, k_self, v_self, o, lse, d_o, anchor, ctx_beg
     return dq, dk, dv, dks, dvs
 
 
-__all__ = ["Shape", "Chunks", "BsxError", "abi_version", "validate_mask", "lpt", "LptResult",
+class Prepared:
+    """A validated call of one C ABI entry point: argument checks and pointer
+    marshalling ran once; each call re-enters the library with the stored arguments
+    on the stream that was current when it was prepared (low host overhead for
+    calls repeated every step)."""
+
+    def __init__(self, fn, args: list, keep: list, chunk_slot: Optional[int] = None):
+        self._fn = fn
+        self._args = args
+        self._keep = keep
+        self._chunk_slot = chunk_slot
+
+    def set_chunks(self, chunks: "Chunks", like: "Chunks") -> None:
+        """Swap the chunk table for another with the same slot count and local length
+        (a new plan over the same buffers)."""
+        if self._chunk_slot is None:
+            raise ValueError("this call takes no chunk table")
+        if chunks.n_slots != like.n_slots or chunks.n_local != like.n_local:
+            raise ValueError("new chunk table does not match the prepared buffers")
+        cc = chunks.c()
+        self._keep.append((chunks, cc))
+        del self._keep[:-8]
+        self._args[self._chunk_slot] = ctypes.byref(cc)
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != 0:
+            check(st)
+
+
+def _prepare(fn, args, keep, chunk_slot=None) -> Prepared:
+    return Prepared(fn, list(args), keep, chunk_slot)
+
+
+def prepare_cost(shape: Shape, anchor, ctx_begin, chunks: Chunks, chunk_cost, mask_err,
+                 counts=None, ws=None) -> Prepared:
+    dev = anchor.device
+    if ws is None:
+        raise ValueError("a prepared call needs its workspace")
+    cost(shape, anchor, ctx_begin, chunks, with_counts=counts is not None, ws=ws,
+         out=(counts, chunk_cost, mask_err), _launch=False)
+    ws = _workspace(cost_workspace_bytes(chunks.n_chunks), dev, ws)
+    sc, cc = shape.c(), chunks.c()
+    args = [ctypes.byref(sc), _ptr(anchor), _ptr(ctx_begin), ctypes.byref(cc), _ptr(counts),
+            _ptr(chunk_cost), _ptr(mask_err), _ptr(ws), ws.numel(), _stream(anchor)]
+    return _prepare(lib().bsx_cost, args, [sc, cc, chunks, anchor, ctx_begin, counts,
+                                           chunk_cost, mask_err, ws], chunk_slot=3)
+
+
+def prepare_attn_fwd(shape: Shape, q, k, v, k_self, v_self, anchor, ctx_begin, chunks: Chunks,
+                     o_part, lse_part, ws) -> Prepared:
+    attn_fwd(shape, q, k, v, k_self, v_self, anchor, ctx_begin, chunks, o_part, lse_part, ws,
+             _launch=False)
+    if ws is None:
+        raise ValueError("a prepared call needs its workspace")
+    sc, cc = shape.c(), chunks.c()
+    args = [ctypes.byref(sc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_self), _ptr(v_self), _ptr(anchor),
+            _ptr(ctx_begin), ctypes.byref(cc), _ptr(o_part), _ptr(lse_part), _ptr(ws), ws.numel(),
+            _stream(q)]
+    return _prepare(lib().bsx_attn_fwd, args, [sc, cc, chunks, q, k, v, k_self, v_self, anchor,
+                                               ctx_begin, o_part, lse_part, ws], chunk_slot=8)
+
+
+def prepare_lse_merge(o_parts, lse_parts, o_out, lse_out) -> Prepared:
+    lse_merge(o_parts, lse_parts, o_out, lse_out, _launch=False)
+    P = int(o_parts.shape[0])
+    d = int(o_parts.shape[-1])
+    n_rows = int(np.prod(lse_parts.shape[1:])) if lse_parts.dim() > 1 else 1
+    args = [P, n_rows, d, _ptr(o_parts), _ptr(lse_parts), _ptr(o_out), _ptr(lse_out),
+            _stream(o_parts)]
+    return _prepare(lib().bsx_lse_merge, args, [o_parts, lse_parts, o_out, lse_out])
+
+
+def prepare_attn_bwd(shape: Shape, q, k, v, k_self, v_self, o, lse, d_o, anchor, ctx_begin,
+                     chunks: Chunks, out, ws) -> Prepared:
+    attn_bwd(shape, q, k, v, k_self, v_self, o, lse, d_o, anchor, ctx_begin, chunks, out, ws,
+             _launch=False)
+    if ws is None or out is None:
+        raise ValueError("a prepared call needs its outputs and workspace")
+    dq, dk, dv, dks, dvs = out
+    sc, cc = shape.c(), chunks.c()
+    args = [ctypes.byref(sc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_self), _ptr(v_self), _ptr(o),
+            _ptr(lse), _ptr(d_o), _ptr(anchor), _ptr(ctx_begin), ctypes.byref(cc), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(dks), _ptr(dvs), _ptr(ws), ws.numel(), _stream(q)]
+    return _prepare(lib().bsx_attn_bwd, args, [sc, cc, chunks, q, k, v, k_self, v_self, o, lse,
+                                               d_o, anchor, ctx_begin, dq, dk, dv, dks, dvs, ws],
+                    chunk_slot=11)
+
+
+__all__ = ["Prepared", "prepare_cost", "prepare_attn_fwd", "prepare_lse_merge",
+           "prepare_attn_bwd", "Shape", "Chunks", "BsxError", "abi_version", "validate_mask", "lpt", "LptResult",
            "cost", "cost_workspace_bytes", "attn_fwd", "fwd_workspace_bytes", "lse_merge",
            "attn_bwd", "bwd_workspace_bytes"]

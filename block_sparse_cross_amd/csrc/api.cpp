@@ -103,12 +103,15 @@ bsx_status check_chunks(const bsx_shape* s, const bsx_chunks* c, bool need_slots
                       c->n_slots);
     }
   }
+  if (total >= (int64_t(1) << 32))
+    return fail(BSX_E_UNSUPPORTED, "local K/V buffer of %lld keys (at most 2^32 - 1)",
+                (long long)total);
   if (n_local) *n_local = total;
   return ok();
 }
 
 // Per-call descriptor of the forward pass: slot_ptr[n_slots + 1] (int32), then the
-// non-empty chunks grouped by slot in chunk index order (ChunkEntry, 8-byte aligned).
+// non-empty chunks grouped by slot in chunk index order (ChunkEntry, 16-byte aligned).
 struct FwdLayout {
   size_t ptr_bytes;
   size_t entries_off;
@@ -118,9 +121,23 @@ struct FwdLayout {
 FwdLayout fwd_layout(int32_t n_slots, int32_t n_chunks) {
   FwdLayout l;
   l.ptr_bytes = sizeof(int32_t) * (size_t(n_slots) + 1);
-  l.entries_off = align_up(l.ptr_bytes, 8);
+  l.entries_off = align_up(l.ptr_bytes, 16);
   l.total = l.entries_off + sizeof(bsx::ChunkEntry) * size_t(n_chunks);
   return l;
+}
+
+// Places a host-built table inline in the kernel arguments when it fits, else
+// uploads it to the workspace on `stream` and points the kernels there.
+hipError_t place_table(const std::vector<uint32_t>& words, void* ws, hipStream_t stream,
+                       bsx::ChunkTable* t) {
+  std::memset(t, 0, sizeof(*t));
+  if (words.size() * 4 <= size_t(bsx::kInlineBytes)) {
+    if (!words.empty()) std::memcpy(t->words, words.data(), words.size() * 4);
+    t->dev = nullptr;
+    return hipSuccess;
+  }
+  t->dev = static_cast<const char*>(ws);
+  return bsx::launch_upload(words.data(), words.size(), static_cast<uint32_t*>(ws), stream);
 }
 
 void build_fwd_descriptor(const bsx_chunks* c, std::vector<uint32_t>* words, int32_t* n_entries) {
@@ -142,7 +159,7 @@ void build_fwd_descriptor(const bsx_chunks* c, std::vector<uint32_t>* words, int
   for (int32_t i = 0; i < nc; ++i) {
     if (c->len[i] <= 0) continue;
     const int32_t s = c->slot ? c->slot[i] : i;
-    ent[fill[s]++] = bsx::ChunkEntry{c->start[i], c->len[i], off[i]};
+    ent[fill[s]++] = bsx::ChunkEntry{c->start[i], uint32_t(c->len[i]), uint32_t(off[i])};
   }
   const size_t used = l.entries_off + sizeof(bsx::ChunkEntry) * ent.size();
   words->assign(align_up(used, 4) / 4, 0u);
@@ -224,7 +241,7 @@ bsx_status bsx_lpt(int32_t n_items, const int64_t* cost, int32_t n_bins, int32_t
 }
 
 size_t bsx_cost_workspace(int32_t n_chunks) {
-  return align_up(sizeof(int64_t) * 2 * size_t(n_chunks < 0 ? 0 : n_chunks), 256) + 256;
+  return align_up(sizeof(bsx::ChunkEntry) * size_t(n_chunks < 0 ? 0 : n_chunks), 256) + 256;
 }
 
 bsx_status bsx_cost(const bsx_shape* shape, const int64_t* anchor, const int64_t* ctx_begin,
@@ -244,15 +261,14 @@ bsx_status bsx_cost(const bsx_shape* shape, const int64_t* anchor, const int64_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   std::vector<uint32_t> words(size_t(chunks->n_chunks) * 4);
   for (int32_t i = 0; i < chunks->n_chunks; ++i) {
-    const int64_t se[2] = {chunks->start[i], chunks->len[i]};
-    std::memcpy(&words[size_t(i) * 4], se, sizeof(se));
+    const bsx::ChunkEntry e{chunks->start[i], uint32_t(chunks->len[i]), 0u};
+    std::memcpy(&words[size_t(i) * 4], &e, sizeof(e));
   }
-  hipError_t e = bsx::launch_upload(words.data(), words.size(), static_cast<uint32_t*>(ws), s);
-  if (e != hipSuccess) return device_status(e, "cost descriptor upload");
   bsx::CostParams p{};
+  hipError_t e = place_table(words, ws, s, &p.table);
+  if (e != hipSuccess) return device_status(e, "cost descriptor upload");
   p.anchor = anchor;
   p.ctx_begin = ctx_begin;
-  p.chunk_se = static_cast<const int64_t*>(ws);
   p.counts = counts;
   p.chunk_cost = chunk_cost;
   p.mask_err = mask_err;
@@ -294,11 +310,12 @@ bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, co
   std::vector<uint32_t> words;
   int32_t n_entries = 0;
   build_fwd_descriptor(chunks, &words, &n_entries);
-  hipError_t e = bsx::launch_upload(words.data(), words.size(), static_cast<uint32_t*>(ws), s);
-  if (e != hipSuccess) return device_status(e, "forward descriptor upload");
   const FwdLayout l = fwd_layout(chunks->n_slots, chunks->n_chunks);
 
   bsx::FwdParams p{};
+  hipError_t e = place_table(words, ws, s, &p.table);
+  if (e != hipSuccess) return device_status(e, "forward descriptor upload");
+  p.entries_off = uint32_t(l.entries_off);
   p.q = q;
   p.k = k;
   p.v = v;
@@ -306,9 +323,6 @@ bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, co
   p.v_self = v_self;
   p.anchor = anchor;
   p.ctx_begin = ctx_begin;
-  p.slot_ptr = static_cast<const int32_t*>(ws);
-  p.entries = reinterpret_cast<const bsx::ChunkEntry*>(static_cast<const char*>(ws) +
-                                                        l.entries_off);
   p.o_part = o_part;
   p.lse_part = lse_part;
   p.ctx_len = shape->ctx_len;
@@ -380,15 +394,16 @@ bsx_status bsx_attn_bwd(const bsx_shape* shape, const void* q, const void* k, co
   std::vector<bsx::ChunkEntry> ent;
   int64_t acc = 0;
   for (int32_t i = 0; i < chunks->n_chunks; ++i) {
-    if (chunks->len[i] > 0) ent.push_back(bsx::ChunkEntry{chunks->start[i], chunks->len[i], acc});
+    if (chunks->len[i] > 0)
+      ent.push_back(bsx::ChunkEntry{chunks->start[i], uint32_t(chunks->len[i]), uint32_t(acc)});
     acc += chunks->len[i];
   }
   std::vector<uint32_t> words(ent.size() * sizeof(bsx::ChunkEntry) / 4);
   if (!ent.empty()) std::memcpy(words.data(), ent.data(), ent.size() * sizeof(bsx::ChunkEntry));
-  hipError_t e = bsx::launch_upload(words.data(), words.size(), static_cast<uint32_t*>(ws), s);
+  bsx::BwdParams p{};
+  hipError_t e = place_table(words, ws, s, &p.table);
   if (e != hipSuccess) return device_status(e, "backward descriptor upload");
   const size_t ent_bytes = align_up(sizeof(bsx::ChunkEntry) * size_t(chunks->n_chunks), 256);
-  bsx::BwdParams p{};
   p.q = q;
   p.k = k;
   p.v = v;
@@ -399,7 +414,6 @@ bsx_status bsx_attn_bwd(const bsx_shape* shape, const void* q, const void* k, co
   p.d_o = d_o;
   p.anchor = anchor;
   p.ctx_begin = ctx_begin;
-  p.entries = static_cast<const bsx::ChunkEntry*>(ws);
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;

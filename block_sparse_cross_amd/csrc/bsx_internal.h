@@ -7,16 +7,31 @@
 
 namespace bsx {
 
-// One non-empty KV chunk as the attention kernels see it: packed positions
-// [start, start + len) stored at local rows [local_off, local_off + len).
+// One KV chunk as the kernels see it: packed positions [start, start + len) stored
+// at local rows [local_off, local_off + len) of the local K/V buffer.
 struct ChunkEntry {
   int64_t start;
-  int64_t len;
-  int64_t local_off;
+  uint32_t len;
+  uint32_t local_off;
 };
 
-// Forward problem as handed to the kernels.  Entries are grouped by output slot:
-// slot s owns entries [slot_ptr[s], slot_ptr[s + 1]), in chunk index order.
+// A small host-built table passed by value in the kernel arguments, so a launch
+// needs no separate copy.  Tables larger than kInlineBytes live in the caller's
+// workspace instead (`dev` non-null), filled by launch_upload on the same stream.
+constexpr int kInlineBytes = 2816;
+struct ChunkTable {
+  const char* dev;
+  uint32_t words[kInlineBytes / 4];
+#ifdef __HIPCC__
+  __device__ const char* base() const {
+    return dev ? dev : reinterpret_cast<const char*>(words);
+  }
+#endif
+};
+
+// Forward problem as handed to the kernels.  The table holds slot_ptr[n_slots + 1]
+// (int32) at byte 0 and the non-empty chunks grouped by slot, in chunk index order,
+// at byte entries_off: slot s owns entries [slot_ptr[s], slot_ptr[s + 1]).
 struct FwdParams {
   const void* q;
   const void* k;
@@ -25,8 +40,6 @@ struct FwdParams {
   const void* v_self;
   const int64_t* anchor;
   const int64_t* ctx_begin;
-  const int32_t* slot_ptr;
-  const ChunkEntry* entries;
   float* o_part;
   float* lse_part;
   int64_t ctx_len;
@@ -39,6 +52,8 @@ struct FwdParams {
   int32_t has_self;
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
+  uint32_t entries_off;
+  ChunkTable table;
 };
 
 struct BwdParams {
@@ -52,7 +67,6 @@ struct BwdParams {
   const void* d_o;
   const int64_t* anchor;
   const int64_t* ctx_begin;
-  const ChunkEntry* entries;  // every non-empty chunk, in chunk index order
   float* dq;
   float* dk;
   float* dv;
@@ -69,12 +83,12 @@ struct BwdParams {
   int32_t has_self;
   float scale;
   float scale_log2;
+  ChunkTable table;           // every non-empty chunk, in chunk index order
 };
 
 struct CostParams {
   const int64_t* anchor;
   const int64_t* ctx_begin;
-  const int64_t* chunk_se;  // [n_chunks][2]: start, len
   int64_t* counts;          // may be null
   int64_t* chunk_cost;
   int32_t* mask_err;
@@ -82,10 +96,11 @@ struct CostParams {
   int32_t n_blocks;
   int32_t block_size;
   int32_t n_chunks;
+  ChunkTable table;         // ChunkEntry per chunk, every chunk, in index order
 };
 
 // Largest payload one upload launch carries in its kernel arguments.
-constexpr int kUploadWords = 480;
+constexpr int kUploadWords = kInlineBytes / 4;
 
 hipError_t launch_upload(const uint32_t* host_words, size_t n_words, uint32_t* dst,
                          hipStream_t stream);

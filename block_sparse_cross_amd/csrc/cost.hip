@@ -35,8 +35,9 @@ __global__ __launch_bounds__(256) void cost_kernel(CostParams p) {
     if (threadIdx.x == 0) *p.mask_err = bad ? 1 : 0;
   }
   if (c >= p.n_chunks) return;
-  const int64_t c0 = p.chunk_se[2 * c];
-  const int64_t c1 = c0 + p.chunk_se[2 * c + 1];
+  const ChunkEntry ce = reinterpret_cast<const ChunkEntry*>(p.table.base())[c];
+  const int64_t c0 = ce.start;
+  const int64_t c1 = c0 + ce.len;
   int64_t total = 0;
   for (int b = 0; b < p.n_blocks; ++b) {
     int64_t lo, hi;

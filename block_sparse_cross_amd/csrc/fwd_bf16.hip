@@ -15,18 +15,19 @@
 // lanes c and c + 32 hold row c, the softmax row max/sum needs one exchange
 // between the two half-waves, and the per-row rescale of O is a per-lane scalar.
 //   S^T:  A = K tile (keys x d) from LDS, B = Q^T (d x rows) kept in registers.
-//   O^T:  A = V^T tile (d x keys) from LDS, B = P^T (keys x rows) taken straight
+//   O^T:  A = V^T (d x keys), read from the row-major V tile with the gfx950
+//         transpose load ds_read_b64_tr_b16, B = P^T (keys x rows) taken straight
 //         from the S^T accumulator after the softmax (bf16).
-// The accumulator holds keys {0-3, 8-11, 16-19, 24-27} + 4 * half of each 32-key
-// block in a lane, so V^T is stored with bits 2 and 3 of the key index swapped
-// inside each 16-key group; then each PV operand is one 16-byte LDS read.
+// The S^T accumulator holds keys {0-3, 8-11, 16-19, 24-27} + 4 * half of each
+// 32-key block in a lane; the V^T operand is read in that same key order, so P^T
+// never moves between lanes.
 //
-// Memory path: K/V tiles of 64 keys are loaded with 16-byte coalesced global reads
-// into registers one tile ahead, V is transposed in registers (v_perm_b32), and
-// both are written to a double-buffered, XOR-swizzled LDS stage (conflict-free
-// MFMA operand reads); one barrier per tile.  Only the first/last tile of a
-// segment and tiles on a row-range boundary take the per-element mask; keys
-// outside every row's range are never loaded (block-sparse skip).
+// Memory path: K/V rows of a 64-key tile are read with 16-byte buffer loads from a
+// per-tile scalar base (keys past the segment end fall outside the buffer range
+// and read as zero), one tile ahead of the compute, and written to a
+// double-buffered LDS stage with padded rows (conflict-free operand reads); one
+// barrier per tile.  Only tiles that cross a segment end or some row's range take
+// the per-element mask; keys outside every row's range are never loaded.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -42,22 +43,31 @@ constexpr int D = 128;
 constexpr int ROWS = 128;
 constexpr int KT = 64;
 constexpr int THREADS = 256;
-constexpr int K_BYTES = KT * D * 2;   // K tile: 64 keys x 256 B
-constexpr int V_BYTES = KT * D * 2;   // V^T tile: 128 dims x 128 B
+constexpr int kXcds = 8;                     // MI355X: 8 XCDs, round-robin dispatch
+constexpr int K_PITCH = 272;                 // bytes per staged K row (256 + 16 pad)
+constexpr int V_PITCH = 288;                 // bytes per staged V row (256 + 32 pad)
+constexpr int K_BYTES = KT * K_PITCH;
+constexpr int V_BYTES = KT * V_PITCH;
 constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// LDS byte offset of the 16-byte chunk `ch` (0..15) of key row `key` in a K tile.
-__device__ inline int k_off(int key, int ch) { return key * 256 + ((ch ^ (key & 7)) << 4); }
-// LDS byte offset of the 16-byte chunk `ch` (0..7) of dim row `d` in a V^T tile.
-__device__ inline int vt_off(int d, int ch) { return d * 128 + ((ch ^ ((d ^ (d >> 3)) & 7)) << 4); }
-// Stored position of key w (0..15) inside its 16-key group: bits 2 and 3 swapped.
-__device__ inline int vt_pos(int w) { return (w & 3) | ((w & 4) << 1) | ((w & 8) >> 1); }
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ inline int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
 
 struct Tile {
   int64_t p0;     // first position
@@ -90,7 +100,8 @@ struct TileWalk {
   }
 };
 
-__global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams p, int n_tiles) {
+__global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_tiles, int n_pairs) {
+  const FwdParams& p = kernel_arg0<FwdParams>();
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
   __shared__ int64_t red[4][4];
 
@@ -98,11 +109,16 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams p, int n
   const int wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
 
-  int bid = blockIdx.x;
-  const int tile_id = n_tiles - 1 - (bid % n_tiles);
-  bid /= n_tiles;
-  const int g = bid % p.n_kv_heads;
-  const int slot = bid / p.n_kv_heads;
+  // Workgroup i runs on XCD i % 8.  All row tiles of one (KV head, slot) pair go to
+  // the same XCD (pair p -> XCD p % 8) so they share that XCD's L2 copy of the
+  // slot's K/V; within an XCD, pairs run one after another, each over its tiles.
+  const int xcd = blockIdx.x % kXcds;
+  const int j = blockIdx.x / kXcds;
+  const int pair = (j / n_tiles) * kXcds + xcd;
+  const int tile_id = n_tiles - 1 - (j % n_tiles);
+  if (pair >= n_pairs) return;
+  const int g = pair % p.n_kv_heads;
+  const int slot = pair / p.n_kv_heads;
   const bool is_self = p.has_self && slot == p.n_slots;
   const int G = p.n_q_heads / p.n_kv_heads;
   const int64_t n_q = int64_t(p.n_blocks) * p.block_size;
@@ -114,10 +130,12 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams p, int n
   const int64_t qi = row_ok ? r / G : 0;
   const int h = g * G + int(row_ok ? r % G : 0);
   int64_t lo = 0, hi = 0;
-  if (row_ok) visible_range(p, is_self, qi / p.block_size, &lo, &hi);
+  if (row_ok)
+    visible_range(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, is_self, qi / p.block_size,
+                  &lo, &hi);
   const bool live = row_ok && lo < hi;
 
-  // ---- workgroup-wide union [mlo, mhi) and intersection [Lmax, Hmin) of live ranges
+  // ---- workgroup-wide union [mlo, mhi) and intersection [lmax, hmin) of live ranges
   {
     int64_t a = live ? lo : INT64_MAX, b = live ? hi : INT64_MIN;
     int64_t c = live ? lo : INT64_MIN, e = live ? hi : INT64_MAX;
@@ -144,11 +162,16 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams p, int n
     lmax = red[w][2] > lmax ? red[w][2] : lmax;
     hmin = red[w][3] < hmin ? red[w][3] : hmin;
   }
+  mlo = uniform64(mlo);
+  mhi = uniform64(mhi);
+  lmax = uniform64(lmax);
+  hmin = uniform64(hmin);
 
   const int64_t orow = (int64_t(slot) * n_q + qi) * p.n_q_heads + h;
 
   TileWalk walk;
-  walk.seg.init(p, slot, is_self, mlo, mhi);
+  walk.seg.init(p.table.dev ? p.table.dev : reinterpret_cast<const char*>(p.table.words),
+                p.entries_off, slot, is_self, mlo, mhi);
   bool have = mlo < mhi && walk.first();
   if (!have) {
     if (row_ok && half == 0) p.lse_part[orow] = -INFINITY;
@@ -158,38 +181,40 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams p, int n
   // ---- Q^T fragments: lane (half, col) holds dims 16t + 8*half .. +8 of its row
   bf16x8 qf[8];
   {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (qi * p.n_q_heads + h) * D;
+    // uniform base at the tile's first query; rows past the end read as zero
+    const int64_t q0 = int64_t(tile_id) * ROWS / G;
+    const int64_t q_bytes = (n_q - q0) * p.n_q_heads * D * 2;
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc(static_cast<const uint16_t*>(p.q) + q0 * p.n_q_heads * D,
+                  uint32_t(q_bytes < 0xffffffffll ? q_bytes : 0xffffffffll));
+    const uint32_t qoff =
+        row_ok ? uint32_t(((qi - q0) * p.n_q_heads + h) * D * 2) + 16 * half : 0x80000000u;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row_ok) x = *reinterpret_cast<const u32x4*>(qrow + 16 * t + 8 * half);
-      qf[t] = __builtin_bit_cast(bf16x8, x);
-    }
+    for (int t = 0; t < 8; ++t)
+      qf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 32 * t,
+                                                                               0, 0));
   }
 
   const uint16_t* kbase = static_cast<const uint16_t*>(is_self ? p.k_self : p.k);
   const uint16_t* vbase = static_cast<const uint16_t*>(is_self ? p.v_self : p.v);
-  const int64_t kstride = int64_t(p.n_kv_heads) * D;
+  const int64_t kstride = int64_t(p.n_kv_heads) * D;      // elements between key rows
+  const uint32_t row_bytes = uint32_t(kstride * 2);
   const int64_t gofs = int64_t(g) * D;
 
-  // staging registers: K rows (tid>>4) + 16i, chunk tid&15; V keys 4*(tid>>4)+i, dims 8*(tid&15)
-  u32x4 kr[4], vr[4];
+  // staging: thread loads key rows ld_row + 16 i, 16-byte chunk ld_ch, of K and V
   const int ld_row = tid >> 4, ld_ch = tid & 15;
+  const uint32_t ld_off = uint32_t(ld_row) * row_bytes + uint32_t(ld_ch) * 16;
+  u32x4 kr[4], vr[4];
 
   auto load_tile = [&](const Tile& t) {
+    // the buffer ends after the tile's last valid key: rows beyond it read as zero
+    const uint32_t bytes = uint32_t(t.nvalid - 1) * row_bytes + D * 2;
+    const __amdgpu_buffer_rsrc_t kb = make_rsrc(kbase + t.l0 * kstride + gofs, bytes);
+    const __amdgpu_buffer_rsrc_t vb = make_rsrc(vbase + t.l0 * kstride + gofs, bytes);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = ld_row + 16 * i;
-      kr[i] = u32x4{0u, 0u, 0u, 0u};
-      if (key < t.nvalid)
-        kr[i] = *reinterpret_cast<const u32x4*>(kbase + (t.l0 + key) * kstride + gofs + 8 * ld_ch);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 4 * ld_row + i;
-      vr[i] = u32x4{0u, 0u, 0u, 0u};
-      if (key < t.nvalid)
-        vr[i] = *reinterpret_cast<const u32x4*>(vbase + (t.l0 + key) * kstride + gofs + 8 * ld_ch);
+      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(kb, ld_off + uint32_t(16 * i) * row_bytes, 0, 0);
+      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vb, ld_off + uint32_t(16 * i) * row_bytes, 0, 0);
     }
   };
 
@@ -198,21 +223,15 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams p, int n
     char* vb = kb + K_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = ld_row + 16 * i;
-      *reinterpret_cast<u32x4*>(kb + k_off(key, ld_ch)) = kr[i];
-    }
-    // V: keys 4*ld_row .. +3 of dims 8*ld_ch .. +7 -> V^T rows d, stored positions sp .. sp+3
-    const int k4 = 4 * ld_row;
-    const int sp = (k4 & ~15) | vt_pos(k4 & 15);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t w0 = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
-      const uint32_t w1 = __builtin_amdgcn_perm(vr[3][e >> 1], vr[2][e >> 1], sel);
-      const int d = 8 * ld_ch + e;
-      *reinterpret_cast<u32x2*>(vb + vt_off(d, sp >> 3) + ((sp & 7) << 1)) = u32x2{w0, w1};
+      *reinterpret_cast<u32x4*>(kb + (ld_row + 16 * i) * K_PITCH + ld_ch * 16) = kr[i];
+      *reinterpret_cast<u32x4*>(vb + (ld_row + 16 * i) * V_PITCH + ld_ch * 16) = vr[i];
     }
   };
+
+  // per-lane LDS read offsets (everything else is an immediate)
+  const int k_rd = col * K_PITCH + half * 16;
+  const int tj = lane & 15, tg = lane >> 4;
+  const int v_rd = (4 * half + (tj >> 2)) * V_PITCH + (16 * (tg & 1) + 4 * (tj & 3)) * 2;
 
   f32x16 acc_o[4];
 #pragma unroll
@@ -236,18 +255,18 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams p, int n
       load_tile(nxt);
     }
 
-    // ---- S^T = K Q^T for the two 32-key blocks of the tile
     const char* kb = smem + stage * STAGE_BYTES;
     const char* vb = kb + K_BYTES;
+
+    // ---- S^T = K Q^T for the two 32-key blocks of the tile
     f32x16 s[2];
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[b2][v] = 0.f;
-      const int key = b2 * 32 + col;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + k_off(key, 2 * t + half));
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + k_rd + b2 * 32 * K_PITCH + 32 * t);
         s[b2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[t],
                                                          s[b2], 0, 0, 0);
       }
@@ -256,14 +275,16 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams p, int n
     // ---- mask (boundary tiles only), online softmax in base 2
     const bool full = cur.nvalid == KT && cur.p0 >= lmax && cur.p0 + KT <= hmin;
     if (!full) {
+      const int64_t dl = lo - cur.p0, dh = hi - cur.p0;
+      const int lo_rel = int(dl < -1 ? -1 : (dl > KT ? KT : dl));
+      const int hi_rel = int(dh < -1 ? -1 : (dh > KT ? KT : dh));
+      const int lim = hi_rel < cur.nvalid ? hi_rel : cur.nvalid;
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = b2 * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          const int64_t pos = cur.p0 + key;
-          const bool vis = key < cur.nvalid && pos >= lo && pos < hi;
-          s[b2][v] = vis ? s[b2][v] : -INFINITY;
+          s[b2][v] = (key >= lo_rel && key < lim) ? s[b2][v] : -INFINITY;
         }
     }
     float mt = -INFINITY;
@@ -271,29 +292,34 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams p, int n
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[b2][v]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m, mt * c2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-    float psum = 0.f;
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
+    // Lazy rescale: keep the reference max until a tile exceeds it by more than
+    // kRescaleSlack (base 2), so exp2 results stay <= 2^kRescaleSlack and the
+    // accumulator is rescaled only when the reference moves.
+    const bool bump = mt > m + kRescaleSlack;
+    if (__any(bump)) {
+      // rows that do not move keep alpha = 1 (also when their reference is still -inf)
+      const float alpha = bump ? __builtin_amdgcn_exp2f(m - mt) : 1.f;  // 0 when m = -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+      m = bump ? mt : m;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float e = __builtin_amdgcn_exp2f(fmaf(s[b2][v], c2, -m_use));
         s[b2][v] = e;
-        psum += e;
+        ps[v & 3] += e;
       }
-    lsum = lsum * alpha + psum;
-    m = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
-    }
+    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T: V^T operand = two transpose loads of 4 keys x 16 dims
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       bf16x8 pf;
@@ -301,10 +327,11 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams p, int n
       for (int e = 0; e < 8; ++e) pf[e] = static_cast<__bf16>(s[u >> 1][8 * (u & 1) + e]);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int d = db * 32 + col;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(vb + vt_off(d, 2 * u + half));
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf,
-                                                             acc_o[db], 0, 0, 0);
+        const char* va = vb + v_rd + 16 * u * V_PITCH + db * 64;
+        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va));
+        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va + 8 * V_PITCH));
+        const bf16x8 a = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, acc_o[db], 0, 0, 0);
       }
     }
 
@@ -341,11 +368,13 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
   const int64_t n_tiles = (n_rows + ROWS - 1) / ROWS;
   const int64_t n_out = int64_t(p.n_slots) + p.has_self;
-  const int64_t grid = n_tiles * p.n_kv_heads * n_out;
+  const int64_t n_pairs = int64_t(p.n_kv_heads) * n_out;
+  const int64_t per_xcd = (n_pairs + kXcds - 1) / kXcds;
+  const int64_t grid = kXcds * per_xcd * n_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fwd_bf16_kernel, dim3(unsigned(grid)), dim3(THREADS), 0, stream, p,
-                     int(n_tiles));
+                     int(n_tiles), int(n_pairs));
   return hipGetLastError();
 }
 

@@ -13,17 +13,30 @@
 
 namespace bsx {
 
+// The kernel's first argument, read in place from the kernarg segment (where it
+// sits at offset 0).  Naming the by-value parameter instead would make the
+// compiler copy the whole struct, inline chunk table included, to scratch.
+template <typename T>
+__device__ inline const T& kernel_arg0() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return *(const T*)__builtin_amdgcn_kernarg_segment_ptr();
+#else
+  return *static_cast<const T*>(nullptr);  // host pass: never executed
+#endif
+}
+
 // Visible range of block `blk` in the slot's position space, clamped to [0, S].
-__device__ inline void visible_range(const FwdParams& p, bool self_slot, int64_t blk,
+__device__ inline void visible_range(const int64_t* anchor, const int64_t* ctx_begin,
+                                     int64_t S, int block_size, bool self_slot, int64_t blk,
                                      int64_t* lo, int64_t* hi) {
   if (self_slot) {
-    *lo = blk * p.block_size;
-    *hi = *lo + p.block_size;
+    *lo = blk * block_size;
+    *hi = *lo + block_size;
     return;
   }
-  int64_t a = p.ctx_begin[blk], z = p.anchor[blk];
-  a = a < 0 ? 0 : (a > p.ctx_len ? p.ctx_len : a);
-  z = z < a ? a : (z > p.ctx_len ? p.ctx_len : z);
+  int64_t a = ctx_begin[blk], z = anchor[blk];
+  a = a < 0 ? 0 : (a > S ? S : a);
+  z = z < a ? a : (z > S ? S : z);
   *lo = a;
   *hi = z;
 }
@@ -42,7 +55,9 @@ struct SegmentWalk {
   int64_t seg1;
   int64_t local0;
 
-  __device__ void init(const FwdParams& p, int slot, bool is_self, int64_t lo, int64_t hi) {
+  // table: slot_ptr (int32) at byte 0, ChunkEntry list at entries_off
+  __device__ void init(const char* table, uint32_t entries_off, int slot, bool is_self,
+                       int64_t lo, int64_t hi) {
     self_slot = is_self;
     minlo = lo;
     maxhi = hi;
@@ -51,9 +66,10 @@ struct SegmentWalk {
       e = 0;
       e_end = 1;
     } else {
-      ent = p.entries;
-      e = p.slot_ptr[slot];
-      e_end = p.slot_ptr[slot + 1];
+      const int32_t* slot_ptr = reinterpret_cast<const int32_t*>(table);
+      ent = reinterpret_cast<const ChunkEntry*>(table + entries_off);
+      e = slot_ptr[slot];
+      e_end = slot_ptr[slot + 1];
     }
   }
 

@@ -32,7 +32,8 @@ constexpr int PAD_Q = QUARTER + 1;    // padded quarter row in LDS
 constexpr int ROW_PITCH = 4 * PAD_Q;  // 132 floats per staged key
 constexpr float kLn2 = 0.6931471805599453f;
 
-__global__ __launch_bounds__(THREADS) void fwd_f32_kernel(FwdParams p, int n_tiles) {
+__global__ __launch_bounds__(THREADS) void fwd_f32_kernel(FwdParams, int n_tiles) {
+  const FwdParams& p = kernel_arg0<FwdParams>();
   __shared__ float sk[KT * ROW_PITCH];
   __shared__ float sv[KT * ROW_PITCH];
   __shared__ int64_t red_lo[THREADS / 64], red_hi[THREADS / 64];
@@ -54,7 +55,9 @@ __global__ __launch_bounds__(THREADS) void fwd_f32_kernel(FwdParams p, int n_til
   const int64_t qi = row_ok ? r / G : 0;
   const int h = g * G + int(row_ok ? r % G : 0);
   int64_t lo = 0, hi = 0;
-  if (row_ok) visible_range(p, is_self, qi / p.block_size, &lo, &hi);
+  if (row_ok)
+    visible_range(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, is_self, qi / p.block_size,
+                  &lo, &hi);
   const bool live = row_ok && lo < hi;
 
   // union of the live rows' ranges
@@ -88,7 +91,8 @@ __global__ __launch_bounds__(THREADS) void fwd_f32_kernel(FwdParams p, int n_til
   const int64_t kstride = int64_t(p.n_kv_heads) * D;
 
   SegmentWalk walk;
-  walk.init(p, slot, is_self, mlo, mhi);
+  walk.init(p.table.dev ? p.table.dev : reinterpret_cast<const char*>(p.table.words),
+            p.entries_off, slot, is_self, mlo, mhi);
   while (mlo < mhi && walk.next()) {
     for (int64_t p0 = walk.seg0; p0 < walk.seg1; p0 += KT) {
       const int nvalid = int(walk.seg1 - p0 < KT ? walk.seg1 - p0 : KT);

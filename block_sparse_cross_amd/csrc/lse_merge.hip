@@ -6,11 +6,12 @@
 // M = max_p LSE_p; partials with LSE_p = -inf are skipped without reading O_p.
 //
 // Bandwidth-bound: the kernel streams every finite partial row once.  A workgroup
-// owns kRowsPerWg consecutive rows.  Phase 1: the four waves split the partials,
-// each lane keeps an online (max, sum) for one row from coalesced LSE loads, and
-// the four partial sums meet in LDS.  Phase 2: head_dim/4 lanes per row each own
-// one float4 of the row and accumulate the weighted partial rows, with the part
-// loop unrolled so several 16-byte loads are in flight per lane.
+// owns kRowsPerWg consecutive rows (few, so thousands of workgroups keep enough
+// loads in flight).  Phase 1: 16 lane groups split the partials, each lane keeps
+// an online (max, sum) for one row from coalesced LSE loads, and the partial sums
+// meet in LDS.  Phase 2: head_dim/4 lanes per row each own one float4 of the row
+// and accumulate the weighted partial rows, with the part loop unrolled so several
+// 16-byte loads are in flight per lane.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -21,7 +22,8 @@ namespace bsx {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerWg = 64;
+constexpr int kRowsPerWg = 16;
+constexpr int kGroups = kThreads / kRowsPerWg;  // partial groups in phase 1
 constexpr int kUnroll = 8;
 
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_t n_rows,
@@ -30,19 +32,19 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
                                                              const float* __restrict__ lse_parts,
                                                              float* __restrict__ o_out,
                                                              float* __restrict__ lse_out) {
-  __shared__ float sh_m[4][kRowsPerWg];
-  __shared__ float sh_s[4][kRowsPerWg];
+  __shared__ float sh_m[kGroups][kRowsPerWg];
+  __shared__ float sh_s[kGroups][kRowsPerWg];
   __shared__ float sh_lse[kRowsPerWg];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
   const int64_t row0 = int64_t(blockIdx.x) * kRowsPerWg;
 
-  // Phase 1: online max/sum of exp over this wave's share of the partials.
+  // Phase 1: online max/sum of exp over this group's share of the partials.
   {
-    const int64_t row = row0 + lane;
+    const int i = tid % kRowsPerWg, grp = tid / kRowsPerWg;
+    const int64_t row = row0 + i;
     float m = -INFINITY, s = 0.f;
     if (row < n_rows) {
-      for (int p = wave; p < n_parts; p += 4) {
+      for (int p = grp; p < n_parts; p += kGroups) {
         const float x = lse_parts[int64_t(p) * n_rows + row];
         if (x == -INFINITY) continue;
         if (x > m) {
@@ -53,17 +55,17 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
         }
       }
     }
-    sh_m[wave][lane] = m;
-    sh_s[wave][lane] = s;
+    sh_m[grp][i] = m;
+    sh_s[grp][i] = s;
   }
   __syncthreads();
   if (tid < kRowsPerWg) {
     float m = -INFINITY;
-    for (int w = 0; w < 4; ++w) m = fmaxf(m, sh_m[w][tid]);
+    for (int w = 0; w < kGroups; ++w) m = fmaxf(m, sh_m[w][tid]);
     float lse = -INFINITY;
     if (m != -INFINITY) {
       float s = 0.f;
-      for (int w = 0; w < 4; ++w)
+      for (int w = 0; w < kGroups; ++w)
         if (sh_m[w][tid] != -INFINITY) s += sh_s[w][tid] * expf(sh_m[w][tid] - m);
       lse = m + logf(s);
     }

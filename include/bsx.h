@@ -82,7 +82,8 @@ typedef struct {
 
 /* KV chunking (host arrays).  Chunk i covers packed positions
  * [start[i], start[i] + len[i]) and sits in the local K/V buffer right after
- * chunks 0 .. i-1, so n_local = sum(len).  Each chunk feeds output slot slot[i]
+ * chunks 0 .. i-1, so n_local = sum(len) (below 2^32; larger local buffers return
+ * BSX_E_UNSUPPORTED).  Each chunk feeds output slot slot[i]
  * (NULL: slot i, which needs n_slots == n_chunks).  Split-KV page, Abstract:
  * key/value chunks stay where they are and are balanced over ranks; a slot is one
  * chunk (per-chunk partials), one LPT bin (virtual rank), or a rank's whole share. */
