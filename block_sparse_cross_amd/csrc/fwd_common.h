@@ -73,6 +73,16 @@ struct SegmentWalk {
     }
   }
 
+  // Walks entries [e0, e1) of an explicit list (all chunks, for the backward pass).
+  __device__ void init_range(const ChunkEntry* list, int e0, int e1, int64_t lo, int64_t hi) {
+    self_slot = false;
+    minlo = lo;
+    maxhi = hi;
+    ent = list;
+    e = e0;
+    e_end = e1;
+  }
+
   // Advances to the next non-empty segment; false when the slot is exhausted.
   __device__ bool next() {
     if (self_slot) {

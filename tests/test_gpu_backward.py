@@ -1,0 +1,160 @@
+"""GPU parity of the attention backward (bf16 inputs, f32 gradients) against the fp64 oracle.
+
+The gradients of the training workload have no tolerance of their own, so each gradient
+tensor must satisfy: max abs error <= 2e-2 * max |reference| and relative L2 error <= 1e-2
+(bf16 operands with f32 accumulation; gradients are small because softmax weights are ~1/n).
+The GPU path takes its merged forward (O, LSE) from its own forward + merge, as a training
+step does; the oracle uses its own fp64 forward.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_cross_amd as bsx
+import oracle
+from parity_helpers import log, shape_of, upload
+from workloads import CONFIGS, make_workload
+from workloads.gen import custom_workload
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 2e-2
+L2_REL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _check(name, got, ref, mask=None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if mask is not None:
+        got, ref = got[mask], ref[mask]
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    scale = np.abs(ref).max()
+    err = np.abs(got - ref).max()
+    l2 = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    log(f"  {name}: max|ref|={scale:.3g} max err={err:.3g} ({err / max(scale, 1e-30):.3g} rel) "
+        f"rel-L2={l2:.3g}")
+    if scale == 0:
+        assert err == 0, name
+        return
+    assert err <= MAX_REL * scale, f"{name}: max error {err} > {MAX_REL} * {scale}"
+    assert l2 <= L2_REL, f"{name}: relative L2 error {l2} > {L2_REL}"
+
+
+def _gpu_forward_backward(wl, k_loc, v_loc, chunks, with_self=True):
+    dev = upload(wl, k_loc, v_loc)
+    shape = shape_of(wl)
+    ks = dev["k_self"] if with_self else None
+    vs = dev["v_self"] if with_self else None
+    o_part, lse_part = bsx.attn_fwd(shape, dev["q"], dev["k"], dev["v"], ks, vs, dev["anchor"],
+                                    dev["ctx_begin"], chunks)
+    o, lse = bsx.lse_merge(o_part, lse_part)
+    grads = bsx.attn_bwd(shape, dev["q"], dev["k"], dev["v"], ks, vs, o, lse, dev["d_o"],
+                         dev["anchor"], dev["ctx_begin"], chunks)
+    torch.cuda.synchronize()
+    return [None if x is None else x.cpu().numpy() for x in grads]
+
+
+CASES = {
+    # name: (S, H_q, H_kv, B, anchors, begins, chunk starts, chunk lens)
+    "gqa4_ragged": (3000, 8, 2, 16, [0, 5, 777, 1500, 2999, 3000], None,
+                    [0, 1000, 1999, 2000], [1000, 999, 1, 1000]),
+    "gqa8_packed": (4096, 32, 4, 16, [100, 1500, 1600, 4000, 2500], [0, 0, 1000, 2400, 2400],
+                    list(range(0, 4096, 512)), [512] * 8),
+    "mha_block5": (700, 4, 4, 5, [3, 100, 650, 699, 700, 0, 350], None, [0, 350], [350, 350]),
+    "gqa2_block8": (900, 8, 4, 8, [899, 450, 10], None, [0, 300, 600], [300, 300, 300]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_backward_small_full(case):
+    S, hq, hk, B, an, be, cs, cl = CASES[case]
+    log(f"backward, {case}")
+    be = [0] * len(an) if be is None else be
+    wl = custom_workload(seed=11, ctx_len=S, n_q_heads=hq, n_kv_heads=hk, block_size=B,
+                         anchor=an, ctx_begin=be, chunk_start=cs, chunk_len=cl, backward=True)
+    k_loc, v_loc = wl.kv_chunks()
+    chunks = bsx.Chunks(cs, cl)
+    dq, dk, dv, dks, dvs = _gpu_forward_backward(wl, k_loc, v_loc, chunks)
+    pos = np.concatenate([np.arange(s, s + c) for s, c in zip(cs, cl)])
+    kg = np.zeros((S, hk, 128), np.float32)
+    vg = np.zeros((S, hk, 128), np.float32)
+    kg[pos], vg[pos] = k_loc, v_loc
+    o, lse = oracle.attention(wl.q, kg, vg, wl.k_self, wl.v_self, wl.anchor, wl.ctx_begin, B)
+    r = oracle.attention_backward(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, B, np.asarray(cs), np.asarray(cl), wl.d_o, o, lse)
+    for name, got, ref in zip(["dq", "dk", "dv", "dk_self", "dv_self"], [dq, dk, dv, dks, dvs], r):
+        _check(name, got, ref)
+
+
+def test_backward_rank_share_without_self():
+    """One rank's non-contiguous chunks, no self keys: local dK/dV exact, dQ is this share."""
+    wl = custom_workload(seed=12, ctx_len=8192, n_q_heads=32, n_kv_heads=8, block_size=16,
+                         anchor=[0, 900, 3000, 5000, 8192, 6100], ctx_begin=[0] * 6,
+                         chunk_start=[4096, 1024, 7168], chunk_len=[1024, 1024, 1024],
+                         backward=True)
+    k_loc, v_loc = wl.kv_chunks()
+    chunks = bsx.Chunks(wl.chunk_start, wl.chunk_len, [0, 0, 0], 1)
+    dq, dk, dv, dks, dvs = _gpu_forward_backward(wl, k_loc, v_loc, chunks, with_self=False)
+    assert dks is None and dvs is None
+    # the GPU's (O, LSE) here are the rank-local partial: the oracle uses the same definition
+    pos = np.concatenate([np.arange(s, s + c) for s, c in zip(wl.chunk_start, wl.chunk_len)])
+    o_p, lse_p = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                      wl.ctx_begin, 16, wl.chunk_start, wl.chunk_len, [0, 0, 0],
+                                      1, with_self=False)
+    r = oracle.attention_backward(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, 16, wl.chunk_start, wl.chunk_len, wl.d_o,
+                                  np.nan_to_num(o_p[0]), lse_p[0], with_self=False)
+    for name, got, ref in zip(["dq", "dk", "dv"], [dq, dk, dv], r[:3]):
+        _check(name, got, ref)
+    assert pos.shape[0] == dk.shape[0]
+
+
+def test_backward_training_workload_one_kv_head():
+    """The full-size training step (8 packed samples, 131072 keys, 16 LPT bins); the oracle
+    computes every gradient of one KV head (all its query heads, keys and draft keys)."""
+    wl = make_workload(CONFIGS[4])
+    c = wl.cfg
+    log(f"backward, {c.name}: blocks={wl.n_blocks}")
+    k_loc, v_loc = wl.kv_chunks()
+    _, cost = oracle.chunk_costs(wl.anchor, wl.ctx_begin, c.block_size, wl.chunk_start,
+                                 wl.chunk_len)
+    bin_of, *_ = oracle.lpt(cost, c.n_bins)
+    chunks = bsx.Chunks(wl.chunk_start, wl.chunk_len, bin_of, c.n_bins)
+    dq, dk, dv, dks, dvs = _gpu_forward_backward(wl, k_loc, v_loc, chunks)
+    g = 5
+    o, lse = oracle.attention(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor, wl.ctx_begin,
+                              c.block_size, groups=[g])
+    r = oracle.attention_backward(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, c.block_size, wl.chunk_start, wl.chunk_len,
+                                  wl.d_o, np.nan_to_num(o), np.nan_to_num(lse, nan=0.0),
+                                  groups=[g])
+    grp = c.group
+    hs = slice(g * grp, (g + 1) * grp)
+    _check("dq[head group]", dq[:, hs], r[0][:, hs])
+    _check("dk[kv head]", dk[:, g], r[1][:, g])
+    _check("dv[kv head]", dv[:, g], r[2][:, g])
+    _check("dk_self[kv head]", dks[:, g], r[3][:, g])
+    _check("dv_self[kv head]", dvs[:, g], r[4][:, g])
+    # keys past the last sample (the padding tail) are seen by no query
+    tail = sum(wl.sample_len)
+    assert np.all(dk[tail:] == 0) and np.all(dv[tail:] == 0)
+
+
+def test_backward_is_deterministic():
+    wl = custom_workload(seed=13, ctx_len=2048, n_q_heads=16, n_kv_heads=4, block_size=16,
+                         anchor=[700, 2048, 1500], ctx_begin=[0, 0, 0], chunk_start=[0, 1024],
+                         chunk_len=[1024, 1024], backward=True)
+    k_loc, v_loc = wl.kv_chunks()
+    chunks = bsx.Chunks(wl.chunk_start, wl.chunk_len)
+    a = _gpu_forward_backward(wl, k_loc, v_loc, chunks)
+    b = _gpu_forward_backward(wl, k_loc, v_loc, chunks)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
