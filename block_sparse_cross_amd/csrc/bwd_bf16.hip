@@ -69,7 +69,7 @@ constexpr int RP = 272;        // LDS pitch (bytes) of a staged Q / dO row
 
 __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BwdParams, int n_ctx_tiles,
                                                               int self_tiles_per_block) {
-  const BwdParams& p = kernel_arg0<BwdParams>();
+  const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
   __shared__ __attribute__((aligned(16))) char sq[RS * RP];
   __shared__ __attribute__((aligned(16))) char sdo[RS * RP];
   __shared__ __attribute__((aligned(16))) float s_lse2[RS];
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BwdParams, int n_c
   const int g = blockIdx.x % Hkv;
   const int t = blockIdx.x / Hkv;
   const bool is_self = t >= n_ctx_tiles;
-  const char* table = p.table.dev ? p.table.dev : reinterpret_cast<const char*>(p.table.words);
+  const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
   const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table);
 
   // ---- this lane's key (both half-waves hold the same key column)
@@ -294,7 +294,7 @@ constexpr int TILE_BYTES = KT * TP;
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 
 __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BwdParams, int n_tiles) {
-  const BwdParams& p = kernel_arg0<BwdParams>();
+  const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
   __shared__ int64_t red[4][4];
 
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BwdParams, int n_til
   const int tile_id = blockIdx.x / Hkv;
   const int64_t n_q = int64_t(p.n_blocks) * B;
   const int64_t n_rows = n_q * G;
-  const char* table = p.table.dev ? p.table.dev : reinterpret_cast<const char*>(p.table.words);
+  const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
   const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table);
 
   const int64_t r = int64_t(tile_id) * QROWS + wave * 32 + col;

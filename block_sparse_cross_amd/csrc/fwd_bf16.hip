@@ -35,6 +35,7 @@
 
 #include "bsx_internal.h"
 #include "fwd_common.h"
+#include "mfma_common.h"
 
 namespace bsx {
 namespace {
@@ -51,23 +52,6 @@ constexpr int V_BYTES = KT * V_PITCH;
 constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-__device__ inline int64_t uniform64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
-  return int64_t((uint64_t(hi) << 32) | lo);
-}
 
 struct Tile {
   int64_t p0;     // first position
@@ -101,7 +85,7 @@ struct TileWalk {
 };
 
 __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_tiles, int n_pairs) {
-  const FwdParams& p = kernel_arg0<FwdParams>();
+  const BSX_KARG FwdParams& p = kernel_arg0<FwdParams>();
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
   __shared__ int64_t red[4][4];
 
@@ -170,7 +154,7 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
   const int64_t orow = (int64_t(slot) * n_q + qi) * p.n_q_heads + h;
 
   TileWalk walk;
-  walk.seg.init(p.table.dev ? p.table.dev : reinterpret_cast<const char*>(p.table.words),
+  walk.seg.init(p.table.dev ? p.table.dev : (const char*)(p.table.words),
                 p.entries_off, slot, is_self, mlo, mhi);
   bool have = mlo < mhi && walk.first();
   if (!have) {

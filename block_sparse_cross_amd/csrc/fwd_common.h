@@ -14,15 +14,32 @@
 namespace bsx {
 
 // The kernel's first argument, read in place from the kernarg segment (where it
-// sits at offset 0).  Naming the by-value parameter instead would make the
-// compiler copy the whole struct, inline chunk table included, to scratch.
-template <typename T>
-__device__ inline const T& kernel_arg0() {
+// sits at offset 0) through a constant-address-space reference: its fields load
+// with scalar instructions as wave-uniform values.  Naming the by-value parameter
+// instead would make the compiler copy the whole struct, inline chunk table
+// included, to scratch.
 #if defined(__HIP_DEVICE_COMPILE__)
-  return *(const T*)__builtin_amdgcn_kernarg_segment_ptr();
+#define BSX_KARG __attribute__((address_space(4)))
+#else
+#define BSX_KARG
+#endif
+template <typename T>
+__device__ inline const BSX_KARG T& kernel_arg0() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return *(const BSX_KARG T*)__builtin_amdgcn_kernarg_segment_ptr();
 #else
   return *static_cast<const T*>(nullptr);  // host pass: never executed
 #endif
+}
+
+// Wave-uniform copies of values read through a generic pointer (chunk tables live
+// either in the kernarg segment or in device memory, so the compiler cannot prove
+// their loads uniform; descriptors built from them must be scalar).
+__device__ inline int32_t uniform32(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline int64_t uniform_i64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
 }
 
 // Visible range of block `blk` in the slot's position space, clamped to [0, S].
@@ -68,8 +85,8 @@ struct SegmentWalk {
     } else {
       const int32_t* slot_ptr = reinterpret_cast<const int32_t*>(table);
       ent = reinterpret_cast<const ChunkEntry*>(table + entries_off);
-      e = slot_ptr[slot];
-      e_end = slot_ptr[slot + 1];
+      e = uniform32(slot_ptr[slot]);
+      e_end = uniform32(slot_ptr[slot + 1]);
     }
   }
 
@@ -95,12 +112,15 @@ struct SegmentWalk {
     }
     while (e < e_end) {
       const ChunkEntry c = ent[e++];
-      const int64_t a = c.start > minlo ? c.start : minlo;
-      const int64_t z = c.start + c.len < maxhi ? c.start + c.len : maxhi;
+      const int64_t start = uniform_i64(c.start);
+      const int64_t len = uniform32(int32_t(c.len)) & 0xffffffffll;
+      const int64_t loff = uniform32(int32_t(c.local_off)) & 0xffffffffll;
+      const int64_t a = start > minlo ? start : minlo;
+      const int64_t z = start + len < maxhi ? start + len : maxhi;
       if (a < z) {
         seg0 = a;
         seg1 = z;
-        local0 = c.local_off + (a - c.start);
+        local0 = loff + (a - start);
         return true;
       }
     }

@@ -33,7 +33,7 @@ constexpr int ROW_PITCH = 4 * PAD_Q;  // 132 floats per staged key
 constexpr float kLn2 = 0.6931471805599453f;
 
 __global__ __launch_bounds__(THREADS) void fwd_f32_kernel(FwdParams, int n_tiles) {
-  const FwdParams& p = kernel_arg0<FwdParams>();
+  const BSX_KARG FwdParams& p = kernel_arg0<FwdParams>();
   __shared__ float sk[KT * ROW_PITCH];
   __shared__ float sv[KT * ROW_PITCH];
   __shared__ int64_t red_lo[THREADS / 64], red_hi[THREADS / 64];
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(THREADS) void fwd_f32_kernel(FwdParams, int n_tiles
   const int64_t kstride = int64_t(p.n_kv_heads) * D;
 
   SegmentWalk walk;
-  walk.init(p.table.dev ? p.table.dev : reinterpret_cast<const char*>(p.table.words),
+  walk.init(p.table.dev ? p.table.dev : (const char*)(p.table.words),
             p.entries_off, slot, is_self, mlo, mhi);
   while (mlo < mhi && walk.next()) {
     for (int64_t p0 = walk.seg0; p0 < walk.seg1; p0 += KT) {

@@ -23,20 +23,25 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
+__device__ inline int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
 // Raw buffer resource over [base, base + bytes): loads past the end read as zero.
+// `base` and `bytes` must be the same in every lane; they are moved to scalar
+// registers explicitly, because after a divergent branch the compiler may no
+// longer prove them uniform and would wrap each load in a per-lane loop.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+  const int64_t b = uniform64(reinterpret_cast<int64_t>(base));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(b), (short)0, (int)n,
                                            0x00020000);
 }
 
 __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-
-__device__ inline int64_t uniform64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
-  return int64_t((uint64_t(hi) << 32) | lo);
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
