@@ -45,6 +45,8 @@ def parse():
                     help="time budget of the oracle's CPU baseline sample (0 skips it)")
     ap.add_argument("--fwd-reps", type=int, default=50,
                     help="event-timed launches of the forward kernel for the roofline")
+    ap.add_argument("--no-merge-bench", action="store_true",
+                    help="skip the standalone 64-set merge measurement")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a reference "
                          "dispatch for scaling HBM byte counters)")
@@ -199,6 +201,40 @@ def time_forward(step: Step, reps: int):
     return start.elapsed_time(end) / reps * 1e-3
 
 
+def merge_bench(device, n_sets: int = 64, rows=(2048, 32), head_dim: int = 128, reps: int = 10,
+                seed: int = 4):
+    """The standalone exact merge of one rank's view at CP size 64: n_sets seeded partial
+    (O, LSE) sets (O ~ N(0,1), LSE ~ N(0,1) + 8, drawn on the device), HBM-bound.
+    Algorithmic bytes per launch: every partial row and LSE read once, the merged row written."""
+    import torch
+    import block_sparse_cross_amd as bsx
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    o = torch.randn((n_sets, *rows, head_dim), generator=g, device=device, dtype=torch.float32)
+    lse = torch.randn((n_sets, *rows), generator=g, device=device, dtype=torch.float32) + 8.0
+    out_o = torch.empty((*rows, head_dim), device=device, dtype=torch.float32)
+    out_l = torch.empty(rows, device=device, dtype=torch.float32)
+    call = bsx.prepare_lse_merge(o, lse, out_o, out_l)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=device)  # 512 MiB > infinity cache
+    call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+    for i in range(reps):
+        flush.zero_()  # cold: the partials are not resident in the infinity cache
+        ev[2 * i].record()
+        call()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    ts = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e-3 for i in range(reps))
+    t = ts[len(ts) // 2]
+    n_rows = rows[0] * rows[1]
+    nbytes = n_sets * n_rows * (head_dim + 1) * 4 + n_rows * (head_dim + 1) * 4
+    del o, lse, flush
+    return {"kernel": "lse_merge_kernel", "sets": n_sets, "shape": [*rows, head_dim],
+            "bound": "hbm", "bytes_per_launch": nbytes, "launch_us": round(t * 1e6, 2),
+            "achieved": round(nbytes / t / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(wl, plan0, seconds: float):
     """The fp64 oracle (forward partials of every slot + merge) on (block, KV head) pairs taken
     in a fixed seeded order until the time budget is spent; useful TFLOP/s of that sample."""
@@ -293,6 +329,7 @@ def main():
                 "traffic": None, "kernel": "fwd_bf16_kernel",
                 "launch_us": round(fwd_s * 1e6, 2),
                 "flops_per_launch": step.fwd_flops}
+    merge = None if args.no_merge_bench else merge_bench(dev)
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(wl, step.plan0, args.cpu_seconds)
@@ -311,6 +348,7 @@ def main():
                    "n_chunks": wl.n_chunks, "slot_mode": c.slot_mode, "n_bins": c.n_bins,
                    "backward": c.backward, "seed": wl.cfg.seed},
         "roofline": roofline,
+        "merge_roofline": merge,
         "cpu_baseline": cpu,
     }
     if c.slot_mode != "per_chunk":

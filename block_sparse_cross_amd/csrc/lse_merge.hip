@@ -9,9 +9,11 @@
 // owns kRowsPerWg consecutive rows (few, so thousands of workgroups keep enough
 // loads in flight).  Phase 1: 16 lane groups split the partials, each lane keeps
 // an online (max, sum) for one row from coalesced LSE loads, and the partial sums
-// meet in LDS.  Phase 2: head_dim/4 lanes per row each own one float4 of the row
-// and accumulate the weighted partial rows, with the part loop unrolled so several
-// 16-byte loads are in flight per lane.
+// meet in LDS.  Phase 2: the weights exp(LSE_p - LSE) of up to kPartsPerPass
+// partials go to LDS, so the O loads that follow depend on nothing in flight;
+// head_dim/4 lanes per row each own one float4 of the row and accumulate the
+// weighted partial rows with the part loop unrolled (several 16-byte loads in
+// flight per lane).  A partial with zero weight (LSE = -inf) is never loaded.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -25,6 +27,7 @@ constexpr int kThreads = 256;
 constexpr int kRowsPerWg = 16;
 constexpr int kGroups = kThreads / kRowsPerWg;  // partial groups in phase 1
 constexpr int kUnroll = 8;
+constexpr int kPartsPerPass = 128;
 
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_t n_rows,
                                                              int head_dim,
@@ -35,6 +38,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
   __shared__ float sh_m[kGroups][kRowsPerWg];
   __shared__ float sh_s[kGroups][kRowsPerWg];
   __shared__ float sh_lse[kRowsPerWg];
+  __shared__ float sh_w[kPartsPerPass][kRowsPerWg];
   const int tid = threadIdx.x;
   const int64_t row0 = int64_t(blockIdx.x) * kRowsPerWg;
 
@@ -75,33 +79,43 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
   }
   __syncthreads();
 
-  // Phase 2: weighted sum of the finite partial rows.
+  // Phase 2: weighted sum of the finite partial rows, kPartsPerPass partials at a
+  // time; with more partials than that, later passes add to the row written so far.
   const int tpr = head_dim >> 2;              // lanes per row, one float4 each
   const int rows_per_pass = kThreads / tpr;
   const int sub = tid / tpr, col = (tid % tpr) * 4;
-  if (sub >= rows_per_pass) return;
-  for (int r = sub; r < kRowsPerWg; r += rows_per_pass) {
-    const int64_t row = row0 + r;
-    if (row >= n_rows) break;
-    const float lse = sh_lse[r];
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lse != -INFINITY) {
-      const float* lp = lse_parts + row;
+  for (int p0 = 0; p0 < n_parts; p0 += kPartsPerPass) {
+    const int np = n_parts - p0 < kPartsPerPass ? n_parts - p0 : kPartsPerPass;
+    __syncthreads();  // previous weights are no longer read
+    for (int idx = tid; idx < np * kRowsPerWg; idx += kThreads) {
+      const int pp = idx / kRowsPerWg, i = idx % kRowsPerWg;
+      const int64_t row = row0 + i;
+      float w = 0.f;
+      if (row < n_rows && sh_lse[i] != -INFINITY) {
+        const float x = lse_parts[int64_t(p0 + pp) * n_rows + row];
+        if (x != -INFINITY) w = expf(x - sh_lse[i]);
+      }
+      sh_w[pp][i] = w;
+    }
+    __syncthreads();
+    if (sub >= rows_per_pass) continue;
+    for (int r = sub; r < kRowsPerWg; r += rows_per_pass) {
+      const int64_t row = row0 + r;
+      if (row >= n_rows) break;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (p0 > 0) acc = *reinterpret_cast<const float4*>(o_out + row * head_dim + col);
       const float* op = o_parts + row * head_dim + col;
-      const int64_t lstride = n_rows, ostride = n_rows * int64_t(head_dim);
-      int p = 0;
-      for (; p + kUnroll <= n_parts; p += kUnroll) {
+      const int64_t ostride = n_rows * int64_t(head_dim);
+      int pp = 0;
+      for (; pp + kUnroll <= np; pp += kUnroll) {
         float w[kUnroll];
         float4 v[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-          const float x = lp[int64_t(p + u) * lstride];
-          w[u] = 0.f;
+          w[u] = sh_w[pp + u][r];
           v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (x != -INFINITY) {
-            w[u] = expf(x - lse);
-            v[u] = *reinterpret_cast<const float4*>(op + int64_t(p + u) * ostride);
-          }
+          if (w[u] != 0.f)
+            v[u] = *reinterpret_cast<const float4*>(op + int64_t(p0 + pp + u) * ostride);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -111,18 +125,17 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
           acc.w = fmaf(w[u], v[u].w, acc.w);
         }
       }
-      for (; p < n_parts; ++p) {
-        const float x = lp[int64_t(p) * lstride];
-        if (x == -INFINITY) continue;
-        const float w = expf(x - lse);
-        const float4 v = *reinterpret_cast<const float4*>(op + int64_t(p) * ostride);
+      for (; pp < np; ++pp) {
+        const float w = sh_w[pp][r];
+        if (w == 0.f) continue;
+        const float4 v = *reinterpret_cast<const float4*>(op + int64_t(p0 + pp) * ostride);
         acc.x = fmaf(w, v.x, acc.x);
         acc.y = fmaf(w, v.y, acc.y);
         acc.z = fmaf(w, v.z, acc.z);
         acc.w = fmaf(w, v.w, acc.w);
       }
+      *reinterpret_cast<float4*>(o_out + row * head_dim + col) = acc;
     }
-    *reinterpret_cast<float4*>(o_out + row * head_dim + col) = acc;
   }
 }
 

@@ -322,7 +322,7 @@ def test_merge_with_empty_partials():
     np.testing.assert_allclose(got_o[fin], ro[fin], atol=1e-5, rtol=0)
 
 
-@pytest.mark.parametrize("P,R,d", [(1, 5, 128), (3, 130, 64), (13, 77, 4), (2, 64, 512)])
+@pytest.mark.parametrize("P,R,d", [(1, 5, 128), (3, 130, 64), (13, 77, 4), (2, 64, 512), (300, 40, 128)])
 def test_merge_shapes(P, R, d):
     rng = np.random.default_rng(P * 1000 + R)
     o = rng.standard_normal((P, R, d)).astype(np.float32)
