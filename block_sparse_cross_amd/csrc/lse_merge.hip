@@ -5,15 +5,15 @@
 //   LSE = M + log sum_p exp(LSE_p - M),   O = sum_p exp(LSE_p - LSE) O_p,
 // M = max_p LSE_p; partials with LSE_p = -inf are skipped without reading O_p.
 //
-// Bandwidth-bound: the kernel streams every finite partial row once.  A workgroup
-// owns kRowsPerWg consecutive rows (few, so thousands of workgroups keep enough
-// loads in flight).  Phase 1: 16 lane groups split the partials, each lane keeps
-// an online (max, sum) for one row from coalesced LSE loads, and the partial sums
-// meet in LDS.  Phase 2: the weights exp(LSE_p - LSE) of up to kPartsPerPass
-// partials go to LDS, so the O loads that follow depend on nothing in flight;
-// head_dim/4 lanes per row each own one float4 of the row and accumulate the
-// weighted partial rows with the part loop unrolled (several 16-byte loads in
-// flight per lane).  A partial with zero weight (LSE = -inf) is never loaded.
+// Bandwidth-bound: every finite partial row is streamed once, with non-temporal
+// loads and stores (read-once data need not displace the caches).  A workgroup owns
+// kRowsPerWg consecutive rows.  Phase 1: the partial LSEs of those rows are read
+// once into LDS while lane groups keep an online (max, sum) per row; the group sums
+// meet in LDS and give each row's LSE.  Phase 2: the LDS values become weights
+// exp(LSE_p - LSE) (0 for an empty partial); head_dim/4 lanes per row each own one
+// float4 column, and every lane accumulates kRowsPerThread rows at once, so each
+// partial is read as one contiguous piece of kRowsPerWg rows.  The loads of the next
+// kUnroll partials are issued before the current ones are consumed.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -23,11 +23,19 @@
 namespace bsx {
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
-constexpr int kRowsPerWg = 16;
-constexpr int kGroups = kThreads / kRowsPerWg;  // partial groups in phase 1
-constexpr int kUnroll = 8;
-constexpr int kPartsPerPass = 128;
+constexpr int kRowsPerThread = 4;
+constexpr int kRowsPerWg = 32;
+constexpr int kGroups = kThreads / kRowsPerWg;  // lane groups of phase 1
+constexpr int kUnroll = 2;                      // partials in flight per row
+constexpr int kPartsPerPass = 128;              // weights held in LDS at once
+static_assert(kThreads % kRowsPerWg == 0, "phase 1 needs whole lane groups");
+
+__device__ inline f32x4 load_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
 
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_t n_rows,
                                                              int head_dim,
@@ -38,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
   __shared__ float sh_m[kGroups][kRowsPerWg];
   __shared__ float sh_s[kGroups][kRowsPerWg];
   __shared__ float sh_lse[kRowsPerWg];
-  __shared__ float sh_w[kPartsPerPass][kRowsPerWg];
+  __shared__ float sh_w[kPartsPerPass][kRowsPerWg];  // partial LSEs, then weights
   const int tid = threadIdx.x;
   const int64_t row0 = int64_t(blockIdx.x) * kRowsPerWg;
 
@@ -50,6 +58,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
     if (row < n_rows) {
       for (int p = grp; p < n_parts; p += kGroups) {
         const float x = lse_parts[int64_t(p) * n_rows + row];
+        if (p < kPartsPerPass) sh_w[p][i] = x;
         if (x == -INFINITY) continue;
         if (x > m) {
           s = s * expf(m - x) + 1.f;
@@ -65,12 +74,12 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
   __syncthreads();
   if (tid < kRowsPerWg) {
     float m = -INFINITY;
-    for (int w = 0; w < kGroups; ++w) m = fmaxf(m, sh_m[w][tid]);
+    for (int g = 0; g < kGroups; ++g) m = fmaxf(m, sh_m[g][tid]);
     float lse = -INFINITY;
     if (m != -INFINITY) {
       float s = 0.f;
-      for (int w = 0; w < kGroups; ++w)
-        if (sh_m[w][tid] != -INFINITY) s += sh_s[w][tid] * expf(sh_m[w][tid] - m);
+      for (int g = 0; g < kGroups; ++g)
+        if (sh_m[g][tid] != -INFINITY) s += sh_s[g][tid] * expf(sh_m[g][tid] - m);
       lse = m + logf(s);
     }
     sh_lse[tid] = lse;
@@ -80,61 +89,75 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
   __syncthreads();
 
   // Phase 2: weighted sum of the finite partial rows, kPartsPerPass partials at a
-  // time; with more partials than that, later passes add to the row written so far.
-  const int tpr = head_dim >> 2;              // lanes per row, one float4 each
+  // time; with more partials than that, later passes reload their LSEs and add to
+  // the rows written so far.
+  const int tpr = head_dim >> 2;  // lanes per row, one float4 each
   const int rows_per_pass = kThreads / tpr;
   const int sub = tid / tpr, col = (tid % tpr) * 4;
+  const int64_t pstride = n_rows * int64_t(head_dim);
   for (int p0 = 0; p0 < n_parts; p0 += kPartsPerPass) {
     const int np = n_parts - p0 < kPartsPerPass ? n_parts - p0 : kPartsPerPass;
-    __syncthreads();  // previous weights are no longer read
+    if (p0 > 0) __syncthreads();  // the previous pass's weights are no longer read
     for (int idx = tid; idx < np * kRowsPerWg; idx += kThreads) {
       const int pp = idx / kRowsPerWg, i = idx % kRowsPerWg;
       const int64_t row = row0 + i;
-      float w = 0.f;
-      if (row < n_rows && sh_lse[i] != -INFINITY) {
-        const float x = lse_parts[int64_t(p0 + pp) * n_rows + row];
-        if (x != -INFINITY) w = expf(x - sh_lse[i]);
-      }
-      sh_w[pp][i] = w;
+      float x = -INFINITY;
+      if (row < n_rows) x = p0 == 0 ? sh_w[pp][i] : lse_parts[int64_t(p0 + pp) * n_rows + row];
+      sh_w[pp][i] = (x == -INFINITY || sh_lse[i] == -INFINITY) ? 0.f : expf(x - sh_lse[i]);
     }
     __syncthreads();
     if (sub >= rows_per_pass) continue;
-    for (int r = sub; r < kRowsPerWg; r += rows_per_pass) {
-      const int64_t row = row0 + r;
-      if (row >= n_rows) break;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (p0 > 0) acc = *reinterpret_cast<const float4*>(o_out + row * head_dim + col);
-      const float* op = o_parts + row * head_dim + col;
-      const int64_t ostride = n_rows * int64_t(head_dim);
-      int pp = 0;
-      for (; pp + kUnroll <= np; pp += kUnroll) {
-        float w[kUnroll];
-        float4 v[kUnroll];
+    for (int rb = sub; rb < kRowsPerWg; rb += rows_per_pass * kRowsPerThread) {
+      int r[kRowsPerThread];
+      bool live[kRowsPerThread];
+      f32x4 acc[kRowsPerThread];
+      const float* src[kRowsPerThread];
+#pragma unroll
+      for (int k = 0; k < kRowsPerThread; ++k) {
+        r[k] = rb + k * rows_per_pass;
+        live[k] = r[k] < kRowsPerWg && row0 + r[k] < n_rows;
+        if (!live[k]) r[k] = 0;  // keeps LDS and pointer arithmetic in range
+        const int64_t off = (row0 + r[k]) * head_dim + col;
+        acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (live[k] && p0 > 0) acc[k] = *reinterpret_cast<const f32x4*>(o_out + off);
+        src[k] = o_parts + int64_t(p0) * pstride + off;
+      }
+      // loads of partial q for every owned row, or zeros where not needed
+      auto fetch = [&](int q, f32x4* v) {
+#pragma unroll
+        for (int k = 0; k < kRowsPerThread; ++k)
+          v[k] = (live[k] && q < np && sh_w[q][r[k]] != 0.f) ? load_nt(src[k] + q * pstride)
+                                                              : f32x4{0.f, 0.f, 0.f, 0.f};
+      };
+      f32x4 cur[kUnroll][kRowsPerThread];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) fetch(u, cur[u]);
+      for (int pp = 0; pp < np; pp += kUnroll) {
+        f32x4 nxt[kUnroll][kRowsPerThread];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) fetch(pp + kUnroll + u, nxt[u]);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-          w[u] = sh_w[pp + u][r];
-          v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (w[u] != 0.f)
-            v[u] = *reinterpret_cast<const float4*>(op + int64_t(p0 + pp + u) * ostride);
+#pragma unroll
+          for (int k = 0; k < kRowsPerThread; ++k) {
+            const float w = pp + u < np ? sh_w[pp + u][r[k]] : 0.f;
+            if (w == 0.f) continue;  // an empty partial's O may hold anything
+            acc[k].x = fmaf(w, cur[u][k].x, acc[k].x);
+            acc[k].y = fmaf(w, cur[u][k].y, acc[k].y);
+            acc[k].z = fmaf(w, cur[u][k].z, acc[k].z);
+            acc[k].w = fmaf(w, cur[u][k].w, acc[k].w);
+          }
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          acc.x = fmaf(w[u], v[u].x, acc.x);
-          acc.y = fmaf(w[u], v[u].y, acc.y);
-          acc.z = fmaf(w[u], v[u].z, acc.z);
-          acc.w = fmaf(w[u], v[u].w, acc.w);
-        }
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+          for (int k = 0; k < kRowsPerThread; ++k) cur[u][k] = nxt[u][k];
       }
-      for (; pp < np; ++pp) {
-        const float w = sh_w[pp][r];
-        if (w == 0.f) continue;
-        const float4 v = *reinterpret_cast<const float4*>(op + int64_t(p0 + pp) * ostride);
-        acc.x = fmaf(w, v.x, acc.x);
-        acc.y = fmaf(w, v.y, acc.y);
-        acc.z = fmaf(w, v.z, acc.z);
-        acc.w = fmaf(w, v.w, acc.w);
-      }
-      *reinterpret_cast<float4*>(o_out + row * head_dim + col) = acc;
+#pragma unroll
+      for (int k = 0; k < kRowsPerThread; ++k)
+        if (live[k])
+          __builtin_nontemporal_store(
+              acc[k], reinterpret_cast<f32x4*>(o_out + (row0 + r[k]) * head_dim + col));
     }
   }
 }
