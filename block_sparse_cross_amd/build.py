@@ -26,6 +26,7 @@ SOURCES = [
     "lse_merge.hip",
     "fwd_f32.hip",
     "fwd_bf16.hip",
+    "fwd_order.hip",
     "bwd_bf16.hip",
 ]
 

@@ -176,6 +176,24 @@ float resolve_scale(const bsx_shape* s) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// bf16 forward launches whose largest slot spans more than this many 64-key tiles
+// run the launch-order pass first.  Measured: slots of 8 chunks x 1024 keys (items of
+// 0 to 128 tiles) gain 10%; one-chunk slots (items of at most 16 tiles, nearly all
+// full) lose 3% to the extra launch.
+constexpr int64_t kOrderMinSlotTiles = 32;
+
+int64_t max_slot_tiles(const bsx_chunks* c) {
+  std::vector<int64_t> tiles(size_t(c->n_slots), 0);
+  for (int32_t i = 0; i < c->n_chunks; ++i) {
+    if (c->len[i] <= 0) continue;
+    tiles[size_t(c->slot ? c->slot[i] : i)] +=
+        (c->len[i] + bsx::kFwdKeyTile - 1) / bsx::kFwdKeyTile;
+  }
+  int64_t m = 0;
+  for (int64_t t : tiles) m = t > m ? t : m;
+  return m;
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,10 +297,26 @@ bsx_status bsx_cost(const bsx_shape* shape, const int64_t* anchor, const int64_t
   return device_status(bsx::launch_cost(p, s), "cost kernel");
 }
 
+// The bf16 launch order (int32 per workgroup) follows the descriptor in the
+// workspace when the problem has at most kOrderMaxItems (row tile, slot) items;
+// sized for a self slot, so it fits either way.
+size_t fwd_order_bytes(const bsx_shape* shape, int32_t n_slots) {
+  if (!shape || shape->dtype != BSX_BF16 || shape->n_kv_heads < 1 || shape->n_blocks < 1)
+    return 0;
+  const int64_t n_out = int64_t(n_slots) + 1;
+  const int64_t n_rows = int64_t(shape->n_blocks) * shape->block_size *
+                         (shape->n_q_heads / shape->n_kv_heads);
+  const int64_t n_tiles = (n_rows + bsx::kFwdRows - 1) / bsx::kFwdRows;
+  if (n_tiles * n_out > bsx::kOrderMaxItems) return 0;
+  return sizeof(int32_t) * size_t(bsx::fwd_bf16_grid(shape->n_blocks, shape->block_size,
+                                                     shape->n_q_heads, shape->n_kv_heads,
+                                                     int32_t(n_out)));
+}
+
 size_t bsx_fwd_workspace(const bsx_shape* shape, const bsx_chunks* chunks) {
-  (void)shape;
   if (!chunks || chunks->n_chunks < 0 || chunks->n_slots < 0) return 0;
-  return align_up(fwd_layout(chunks->n_slots, chunks->n_chunks).total, 256);
+  const size_t table = align_up(fwd_layout(chunks->n_slots, chunks->n_chunks).total, 256);
+  return table + align_up(fwd_order_bytes(shape, chunks->n_slots), 256);
 }
 
 bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, const void* v,
@@ -335,7 +369,22 @@ bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, co
   p.has_self = has_self;
   p.scale = resolve_scale(shape);
   p.scale_log2 = p.scale * kLog2e;
-  e = shape->dtype == BSX_BF16 ? bsx::launch_fwd_bf16(p, s) : bsx::launch_fwd_f32(p, s);
+  p.order = nullptr;
+  if (shape->dtype == BSX_BF16) {
+    // The ordering pass costs a few microseconds of latency; it pays off when items
+    // can differ widely in length, i.e. when a slot holds many key tiles.
+    if (max_slot_tiles(chunks) > kOrderMinSlotTiles &&
+        fwd_order_bytes(shape, chunks->n_slots) > 0) {
+      int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                                  align_up(l.total, 256));
+      e = bsx::launch_fwd_order(p, order, s);
+      if (e != hipSuccess) return device_status(e, "forward launch-order kernel");
+      p.order = order;
+    }
+    e = bsx::launch_fwd_bf16(p, s);
+  } else {
+    e = bsx::launch_fwd_f32(p, s);
+  }
   return device_status(e, "forward kernel");
 }
 

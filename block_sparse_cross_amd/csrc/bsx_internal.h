@@ -29,6 +29,15 @@ struct ChunkTable {
 #endif
 };
 
+// bf16 forward work decomposition: one workgroup per (kFwdRows query rows of a KV
+// head, KV head, slot), keys visited in tiles of kFwdKeyTile; workgroup i runs on
+// XCD i % kXcds (MI355X dispatches workgroups round-robin over its 8 XCDs).
+constexpr int kFwdRows = 128;
+constexpr int kFwdKeyTile = 64;
+constexpr int kXcds = 8;
+// The launch-order pass handles at most this many (row tile, output slot) items.
+constexpr int kOrderMaxItems = 32768;
+
 // Forward problem as handed to the kernels.  The table holds slot_ptr[n_slots + 1]
 // (int32) at byte 0 and the non-empty chunks grouped by slot, in chunk index order,
 // at byte entries_off: slot s owns entries [slot_ptr[s], slot_ptr[s + 1]).
@@ -53,6 +62,7 @@ struct FwdParams {
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
   uint32_t entries_off;
+  const int32_t* order;  // bf16 launch order (workgroup -> item), or null: natural order
   ChunkTable table;
 };
 
@@ -106,6 +116,12 @@ hipError_t launch_upload(const uint32_t* host_words, size_t n_words, uint32_t* d
                          hipStream_t stream);
 hipError_t launch_cost(const CostParams& p, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+// Workgroups of the bf16 forward launch (the length of its launch-order array).
+int64_t fwd_bf16_grid(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
+                      int32_t n_kv_heads, int32_t n_out);
+// Fills `order` (fwd_bf16_grid entries) with the forward's workgroup -> item map,
+// heaviest items first within each XCD; p.order is ignored.
+hipError_t launch_fwd_order(const FwdParams& p, int32_t* order, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
                             const float* o_parts, const float* lse_parts, float* o_out,

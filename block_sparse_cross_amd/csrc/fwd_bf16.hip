@@ -41,10 +41,9 @@ namespace bsx {
 namespace {
 
 constexpr int D = 128;
-constexpr int ROWS = 128;
-constexpr int KT = 64;
+constexpr int ROWS = kFwdRows;
+constexpr int KT = kFwdKeyTile;
 constexpr int THREADS = 256;
-constexpr int kXcds = 8;                     // MI355X: 8 XCDs, round-robin dispatch
 constexpr int K_PITCH = 272;                 // bytes per staged K row (256 + 16 pad)
 constexpr int V_PITCH = 288;                 // bytes per staged V row (256 + 32 pad)
 constexpr int K_BYTES = KT * K_PITCH;
@@ -95,12 +94,21 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
 
   // Workgroup i runs on XCD i % 8.  All row tiles of one (KV head, slot) pair go to
   // the same XCD (pair p -> XCD p % 8) so they share that XCD's L2 copy of the
-  // slot's K/V; within an XCD, pairs run one after another, each over its tiles.
-  const int xcd = blockIdx.x % kXcds;
-  const int j = blockIdx.x / kXcds;
-  const int pair = (j / n_tiles) * kXcds + xcd;
-  const int tile_id = n_tiles - 1 - (j % n_tiles);
-  if (pair >= n_pairs) return;
+  // slot's K/V.  With a launch order, each XCD's items run heaviest first; without
+  // one, pairs run one after another, each over its tiles.
+  int pair, tile_id;
+  if (p.order) {
+    const int code = p.order[blockIdx.x];
+    if (code < 0) return;
+    pair = code / n_tiles;
+    tile_id = code - pair * n_tiles;
+  } else {
+    const int xcd = blockIdx.x % kXcds;
+    const int j = blockIdx.x / kXcds;
+    pair = (j / n_tiles) * kXcds + xcd;
+    tile_id = n_tiles - 1 - (j % n_tiles);
+    if (pair >= n_pairs) return;
+  }
   const int g = pair % p.n_kv_heads;
   const int slot = pair / p.n_kv_heads;
   const bool is_self = p.has_self && slot == p.n_slots;
@@ -118,6 +126,24 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
     visible_range(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, is_self, qi / p.block_size,
                   &lo, &hi);
   const bool live = row_ok && lo < hi;
+
+  // ---- Q^T fragments (issued first: they depend on nothing below): lane (half, col)
+  // holds dims 16t + 8*half .. +8 of its row
+  bf16x8 qf[8];
+  {
+    // uniform base at the tile's first query; rows past the end read as zero
+    const int64_t q0 = int64_t(tile_id) * ROWS / G;
+    const int64_t q_bytes = (n_q - q0) * p.n_q_heads * D * 2;
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc(static_cast<const uint16_t*>(p.q) + q0 * p.n_q_heads * D,
+                  uint32_t(q_bytes < 0xffffffffll ? q_bytes : 0xffffffffll));
+    const uint32_t qoff =
+        row_ok ? uint32_t(((qi - q0) * p.n_q_heads + h) * D * 2) + 16 * half : 0x80000000u;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      qf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 32 * t,
+                                                                               0, 0));
+  }
 
   // ---- workgroup-wide union [mlo, mhi) and intersection [lmax, hmin) of live ranges
   {
@@ -160,23 +186,6 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
   if (!have) {
     if (row_ok && half == 0) p.lse_part[orow] = -INFINITY;
     return;
-  }
-
-  // ---- Q^T fragments: lane (half, col) holds dims 16t + 8*half .. +8 of its row
-  bf16x8 qf[8];
-  {
-    // uniform base at the tile's first query; rows past the end read as zero
-    const int64_t q0 = int64_t(tile_id) * ROWS / G;
-    const int64_t q_bytes = (n_q - q0) * p.n_q_heads * D * 2;
-    const __amdgpu_buffer_rsrc_t qr =
-        make_rsrc(static_cast<const uint16_t*>(p.q) + q0 * p.n_q_heads * D,
-                  uint32_t(q_bytes < 0xffffffffll ? q_bytes : 0xffffffffll));
-    const uint32_t qoff =
-        row_ok ? uint32_t(((qi - q0) * p.n_q_heads + h) * D * 2) + 16 * half : 0x80000000u;
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      qf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 32 * t,
-                                                                               0, 0));
   }
 
   const uint16_t* kbase = static_cast<const uint16_t*>(is_self ? p.k_self : p.k);
@@ -347,14 +356,22 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
 
 }  // namespace
 
+int64_t fwd_bf16_grid(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
+                      int32_t n_kv_heads, int32_t n_out) {
+  const int64_t n_rows = int64_t(n_blocks) * block_size * (n_q_heads / n_kv_heads);
+  const int64_t n_tiles = (n_rows + ROWS - 1) / ROWS;
+  const int64_t per_xcd = (int64_t(n_kv_heads) * n_out + kXcds - 1) / kXcds;
+  return kXcds * per_xcd * n_tiles;
+}
+
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const int G = p.n_q_heads / p.n_kv_heads;
   const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
   const int64_t n_tiles = (n_rows + ROWS - 1) / ROWS;
   const int64_t n_out = int64_t(p.n_slots) + p.has_self;
   const int64_t n_pairs = int64_t(p.n_kv_heads) * n_out;
-  const int64_t per_xcd = (n_pairs + kXcds - 1) / kXcds;
-  const int64_t grid = kXcds * per_xcd * n_tiles;
+  const int64_t grid = fwd_bf16_grid(p.n_blocks, p.block_size, p.n_q_heads, p.n_kv_heads,
+                                     int32_t(n_out));
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fwd_bf16_kernel, dim3(unsigned(grid)), dim3(THREADS), 0, stream, p,

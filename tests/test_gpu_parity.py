@@ -187,6 +187,35 @@ def test_forward_bf16_full_size_sampled(idx):
     compare_partials(mo.cpu().numpy(), ml.cpu().numpy(), uo, ul, tol_o, tol_l, "merged")
 
 
+def test_forward_launch_order_full():
+    """Slots of several chunks (more than 32 key tiles each) take the launch-order pass:
+    8 KV heads, 5 slots of 8 chunks, 13 row tiles, items from empty to full; compared in
+    full, so an item dropped or run twice by the reordering shows up."""
+    S, n_chunks, n_slots = 20480, 40, 5
+    rng = np.random.default_rng(21)
+    n_blocks = 26
+    anchor = rng.integers(0, S + 1, n_blocks)
+    anchor[:3] = [0, S, 65]
+    begin = np.minimum(rng.integers(0, S // 2, n_blocks), anchor)
+    starts = list(range(0, S, S // n_chunks))
+    lens = [S // n_chunks] * n_chunks
+    wl = custom_workload(seed=22, ctx_len=S, n_q_heads=32, n_kv_heads=8, block_size=16,
+                         anchor=anchor.tolist(), ctx_begin=begin.tolist(), chunk_start=starts,
+                         chunk_len=lens)
+    k_loc, v_loc = wl.kv_chunks()
+    dev = upload(wl, k_loc, v_loc)
+    slot_of = np.arange(n_chunks) % n_slots
+    ch = bsx.Chunks(starts, lens, slot_of.tolist(), n_slots)
+    log(f"forward bf16, launch-order case: {n_blocks} blocks, {n_slots} slots of 8 chunks")
+    o, lse = bsx.attn_fwd(shape_of(wl), dev["q"], dev["k"], dev["v"], dev["k_self"],
+                          dev["v_self"], dev["anchor"], dev["ctx_begin"], ch)
+    ro, rl = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, 16, np.asarray(starts), np.asarray(lens),
+                                  slot_of, n_slots, with_self=True)
+    tol_o, tol_l = tolerances("bf16")
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_o, tol_l, "partials")
+
+
 # ----------------------------------------------------------------------------- edge cases
 
 EDGE_CASES = {
