@@ -280,6 +280,36 @@ def cpu_baseline(wl, plan0, seconds: float):
                       f"workload, {dt:.1f} s"}
 
 
+# Sources of the forward kernel; the recorded HBM traffic is valid only for them.
+FWD_SOURCES = ["block_sparse_cross_amd/csrc/fwd_bf16.hip", "block_sparse_cross_amd/csrc/fwd_common.h",
+               "block_sparse_cross_amd/csrc/mfma_common.h", "block_sparse_cross_amd/csrc/bsx_internal.h"]
+
+
+def fwd_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in FWD_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per forward launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the elementwise-kernel calibration), or None when
+    there is none for this workload or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"fwd_bf16_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic_record: "):
+                rec = json.loads(line[len("traffic_record: "):])
+                if rec.get("sources_sha256") == fwd_sources_sha256():
+                    return rec["bytes_per_launch"]
+    return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -296,11 +326,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.calibrate_copy_mib > 0:
+        # a plain elementwise kernel of known traffic (reads and writes N MiB with
+        # ordinary loads and stores), the reference for the HBM byte counters
         n = args.calibrate_copy_mib << 18  # float32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
     cfg = get_config(args.workload)
@@ -326,7 +358,7 @@ def main():
     achieved = step.fwd_flops / fwd_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "kernel": "fwd_bf16_kernel",
+                "traffic": recorded_traffic(cfg.name), "kernel": "fwd_bf16_kernel",
                 "launch_us": round(fwd_s * 1e6, 2),
                 "flops_per_launch": step.fwd_flops}
     merge = None if args.no_merge_bench else merge_bench(dev)
