@@ -411,7 +411,9 @@ size_t bsx_bwd_workspace(const bsx_shape* shape, const bsx_chunks* chunks) {
   const size_t ent = align_up(sizeof(bsx::ChunkEntry) * size_t(chunks->n_chunks), 256);
   const size_t delta =
       align_up(sizeof(float) * size_t(shape->n_blocks) * shape->block_size * shape->n_q_heads, 256);
-  return ent + delta + 256;
+  const bsx::DqLayout l = bsx::bwd_dq_layout(shape->n_blocks, shape->block_size,
+                                             shape->n_q_heads, shape->n_kv_heads);
+  return ent + delta + align_up(l.plan_bytes, 256) + align_up(l.part_bytes, 256) + 256;
 }
 
 bsx_status bsx_attn_bwd(const bsx_shape* shape, const void* q, const void* k, const void* v,
@@ -469,6 +471,13 @@ bsx_status bsx_attn_bwd(const bsx_shape* shape, const void* q, const void* k, co
   p.dk_self = dk_self;
   p.dv_self = dv_self;
   p.delta = reinterpret_cast<float*>(static_cast<char*>(ws) + ent_bytes);
+  const size_t delta_bytes =
+      align_up(sizeof(float) * size_t(shape->n_blocks) * shape->block_size * shape->n_q_heads, 256);
+  const bsx::DqLayout dl = bsx::bwd_dq_layout(shape->n_blocks, shape->block_size,
+                                              shape->n_q_heads, shape->n_kv_heads);
+  p.dq_plan = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ent_bytes + delta_bytes);
+  p.dq_part = reinterpret_cast<float*>(static_cast<char*>(ws) + ent_bytes + delta_bytes +
+                                       align_up(dl.plan_bytes, 256));
   p.ctx_len = shape->ctx_len;
   p.n_local = n_local;
   p.n_entries = int32_t(ent.size());

@@ -83,6 +83,8 @@ struct BwdParams {
   float* dk_self;
   float* dv_self;
   float* delta;               // workspace [N_q][H_q]: rowsum(dO * O)
+  int32_t* dq_plan;           // workspace: dQ work split (bwd_dq_layout)
+  float* dq_part;             // workspace: partial dQ of split row tiles
   int64_t ctx_len;
   int64_t n_local;
   int32_t n_entries;
@@ -126,6 +128,21 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
                             const float* o_parts, const float* lse_parts, float* o_out,
                             float* lse_out, hipStream_t stream);
+// dQ work split: the row tiles (kDqRows query rows of one KV head) are cut into
+// pieces of P key tiles, P chosen so the launch has about kDqTargetWgs workgroups.
+constexpr int kDqRows = 128;
+constexpr int kDqTargetWgs = 2048;
+constexpr int kDqMinPieceTiles = 8;
+struct DqLayout {
+  int64_t n_tiles;        // row tiles per KV head
+  int64_t cap;            // bound on the number of pieces
+  int64_t part_slots;     // bound on the pieces of split row tiles
+  size_t plan_bytes;      // int32: header[4], count[n_tiles], sbase[n_tiles],
+                          // piece_tile[cap], piece_j[cap], multi_tile[n_tiles]
+  size_t part_bytes;      // f32: part_slots x H_kv x kDqRows x 128
+};
+DqLayout bwd_dq_layout(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
+                       int32_t n_kv_heads);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 
 }  // namespace bsx

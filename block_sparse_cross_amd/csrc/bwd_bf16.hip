@@ -20,7 +20,11 @@
 //          whose only rows are their block's.
 //   dq:    query-major, shaped like the forward kernel: 128 rows per workgroup,
 //          K/V tiles of 64 keys in LDS; S^T = K Q^T and dP^T = V dO^T put rows in
-//          lane columns, dQ^T += K^T dS^T reads K^T with transpose loads.
+//          lane columns, dQ^T += K^T dS^T reads K^T with transpose loads.  A
+//          planning pass cuts each row tile's key walk into pieces of P tiles (about
+//          kDqTargetWgs workgroups in all: draft blocks see very different context
+//          lengths); a row tile of one piece writes dQ directly, the pieces of a split
+//          row tile write partial sums that a reduce kernel adds in piece order.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -70,11 +74,12 @@ constexpr int RP = 272;        // LDS pitch (bytes) of a staged Q / dO row
 __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BwdParams, int n_ctx_tiles,
                                                               int self_tiles_per_block) {
   const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
-  __shared__ __attribute__((aligned(16))) char sq[RS * RP];
-  __shared__ __attribute__((aligned(16))) char sdo[RS * RP];
-  __shared__ __attribute__((aligned(16))) float s_lse2[RS];
-  __shared__ __attribute__((aligned(16))) float s_delta[RS];
+  __shared__ __attribute__((aligned(16))) char sq[2][RS * RP];
+  __shared__ __attribute__((aligned(16))) char sdo[2][RS * RP];
+  __shared__ __attribute__((aligned(16))) float s_lse2[2][RS];
+  __shared__ __attribute__((aligned(16))) float s_delta[2][RS];
   __shared__ int s_blocks[THREADS];
+  __shared__ int64_t s_blo[THREADS], s_bhi[THREADS];
   __shared__ int s_wcount[4];
   __shared__ int64_t s_red[4][2];
 
@@ -165,23 +170,63 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BwdParams, int n_c
   const int tr_rd = tr_lane_offset(lane, RP);     // transpose reads of Q^T / dO^T
   const int ld_row = tid >> 3, ld_ch = (tid & 7) * 2;  // staging: row, first of 2 chunks
 
-  // ---- walk the draft blocks whose visible range reaches these keys
+  // ---- walk the draft blocks whose visible range reaches these keys, as a sequence
+  // of (block, 32-row sub-tile) steps; the Q / dO / LSE / D rows of step j + 1 are
+  // loaded into registers while step j computes, then stored to the other LDS stage
+  const int nr = B * G;                         // query rows of one draft block
+  const int nsub = (nr + RS - 1) / RS;
   const int scan_begin = is_self ? self_block : 0;
   const int scan_end = is_self ? self_block + 1 : p.n_blocks;
-  for (int wb = scan_begin; wb < scan_end && pmin <= pmax; wb += THREADS) {
-    // ordered compaction of the hit blocks of this window into s_blocks
-    const int b = wb + tid;
-    bool hit = false;
-    if (b < scan_end) {
-      if (is_self) {
-        hit = true;
-      } else {
-        int64_t lo, hi;
-        visible_range(p.anchor, p.ctx_begin, p.ctx_len, B, false, b, &lo, &hi);
-        hit = lo < hi && lo <= pmax && hi > pmin;
+  u32x4 st_q[2], st_do[2];
+  float st_l2 = INFINITY, st_dl = 0.f;
+  // loads step j of the current window into the staging registers
+  auto load_step = [&](int j) {
+    const int blk = s_blocks[j / nsub];
+    const int rr = (j % nsub) * RS + ld_row;
+    const bool ok = rr < nr;
+    const int64_t r = int64_t(blk) * nr + rr;
+    const int64_t q = ok ? r / G : 0;
+    const int h = g * G + int(ok ? r % G : 0);
+    const int64_t base = (q * Hq + h) * D;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + base;
+    const uint16_t* drow = static_cast<const uint16_t*>(p.d_o) + base;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      st_q[c] = u32x4{0u, 0u, 0u, 0u};
+      st_do[c] = u32x4{0u, 0u, 0u, 0u};
+      if (ok) {
+        st_q[c] = *reinterpret_cast<const u32x4*>(qrow + (ld_ch + c) * 8);
+        st_do[c] = *reinterpret_cast<const u32x4*>(drow + (ld_ch + c) * 8);
       }
     }
+    if ((tid & 7) == 0) {
+      st_l2 = ok && q < n_q ? row_lse2(p.lse[q * Hq + h]) : INFINITY;
+      st_dl = ok && q < n_q ? p.delta[q * Hq + h] : 0.f;
+    }
+  };
+  auto store_step = [&](int stage) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      *reinterpret_cast<u32x4*>(sq[stage] + ld_row * RP + (ld_ch + c) * 16) = st_q[c];
+      *reinterpret_cast<u32x4*>(sdo[stage] + ld_row * RP + (ld_ch + c) * 16) = st_do[c];
+    }
+    if ((tid & 7) == 0) {
+      s_lse2[stage][ld_row] = st_l2;
+      s_delta[stage][ld_row] = st_dl;
+    }
+  };
+
+  for (int wb = scan_begin; wb < scan_end && pmin <= pmax; wb += THREADS) {
+    // ordered compaction of the hit blocks of this window (and their ranges)
+    const int b = wb + tid;
+    bool hit = false;
+    int64_t blo = 0, bhi = 0;
+    if (b < scan_end) {
+      visible_range(p.anchor, p.ctx_begin, p.ctx_len, B, is_self, b, &blo, &bhi);
+      hit = is_self || (blo < bhi && blo <= pmax && bhi > pmin);
+    }
     const uint64_t ball = __ballot(hit);
+    __syncthreads();  // the previous window is done with s_blocks and the stages
     if (lane == 0) s_wcount[wave] = __popcll(ball);
     __syncthreads();
     int before = 0, total = 0;
@@ -189,83 +234,65 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BwdParams, int n_c
       before += w < wave ? s_wcount[w] : 0;
       total += s_wcount[w];
     }
-    if (hit) s_blocks[before + __popcll(ball & ((uint64_t(1) << lane) - 1))] = b;
+    if (hit) {
+      const int at = before + __popcll(ball & ((uint64_t(1) << lane) - 1));
+      s_blocks[at] = b;
+      s_blo[at] = blo;
+      s_bhi[at] = bhi;
+    }
     __syncthreads();
 
-    for (int i = 0; i < total; ++i) {
-      const int blk = s_blocks[i];
-      int64_t lo, hi;
-      visible_range(p.anchor, p.ctx_begin, p.ctx_len, B, is_self, blk, &lo, &hi);
-      const bool key_vis = kvalid && kpos >= lo && kpos < hi;
-      const bool wave_on = __any(key_vis);
-      const int64_t r0 = int64_t(blk) * B * G;
-      const int nr = B * G;
-      for (int rs = 0; rs < nr; rs += RS) {
-        // stage rows r0 + rs .. + RS of Q, dO, LSE, D
-        {
-          const int rr = rs + ld_row;
-          const bool ok = rr < nr;
-          const int64_t r = r0 + rr;
-          const int64_t q = ok ? r / G : 0;
-          const int h = g * G + int(ok ? r % G : 0);
-          const int64_t base = (q * Hq + h) * D;
-          const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + base;
-          const uint16_t* drow = static_cast<const uint16_t*>(p.d_o) + base;
+    const int nseq = total * nsub;
+    if (nseq > 0) {
+      load_step(0);
+      store_step(0);
+    }
+    __syncthreads();
+    for (int j = 0; j < nseq; ++j) {
+      const int stage = j & 1;
+      if (j + 1 < nseq) load_step(j + 1);
+      const int bi = j / nsub;
+      const bool key_vis = kvalid && kpos >= s_blo[bi] && kpos < s_bhi[bi];
+      if (__any(key_vis)) {
+        const char* q_s = sq[stage];
+        const char* do_s = sdo[stage];
+        f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int ch = ld_ch + c;
-            u32x4 qv = {0u, 0u, 0u, 0u}, dv4 = {0u, 0u, 0u, 0u};
-            if (ok) {
-              qv = *reinterpret_cast<const u32x4*>(qrow + ch * 8);
-              dv4 = *reinterpret_cast<const u32x4*>(drow + ch * 8);
-            }
-            *reinterpret_cast<u32x4*>(sq + ld_row * RP + ch * 16) = qv;
-            *reinterpret_cast<u32x4*>(sdo + ld_row * RP + ch * 16) = dv4;
-          }
-          if ((tid & 7) == 0) {
-            s_lse2[ld_row] = ok && q < n_q ? row_lse2(p.lse[q * Hq + h]) : INFINITY;
-            s_delta[ld_row] = ok && q < n_q ? p.delta[q * Hq + h] : 0.f;
+        for (int k = 0; k < 8; ++k) {
+          sacc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(q_s + q_rd + 32 * k)),
+                           kf[k], sacc);
+          dpacc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(do_s + q_rd + 32 * k)),
+                            vf[k], dpacc);
+        }
+        f32x16 pm, ds;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float4 l4 = *reinterpret_cast<const float4*>(s_lse2[stage] + 8 * a + 4 * half);
+          const float4 d4 = *reinterpret_cast<const float4*>(s_delta[stage] + 8 * a + 4 * half);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * a + e;
+            const float pv =
+                key_vis ? __builtin_amdgcn_exp2f(fmaf(sacc[v], c2, -lv[e])) : 0.f;
+            pm[v] = pv;
+            ds[v] = pv * (dpacc[v] - dd[e]);
           }
         }
-        __syncthreads();
-        if (wave_on) {
-          f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            sacc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(sq + q_rd + 32 * k)),
-                             kf[k], sacc);
-            dpacc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(sdo + q_rd + 32 * k)),
-                              vf[k], dpacc);
-          }
-          f32x16 pm, ds;
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 pb = pack_bf16(pm, u);
+          const bf16x8 sb = pack_bf16(ds, u);
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const float4 l4 = *reinterpret_cast<const float4*>(s_lse2 + 8 * a + 4 * half);
-            const float4 d4 = *reinterpret_cast<const float4*>(s_delta + 8 * a + 4 * half);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int v = 4 * a + e;
-              const float pv =
-                  key_vis ? __builtin_amdgcn_exp2f(fmaf(sacc[v], c2, -lv[e])) : 0.f;
-              pm[v] = pv;
-              ds[v] = pv * (dpacc[v] - dd[e]);
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bf16x8 pb = pack_bf16(pm, u);
-            const bf16x8 sb = pack_bf16(ds, u);
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-              dv[db] = mfma_bf16(tr_operand(sdo + tr_rd, RP, u, db * 64), pb, dv[db]);
-              dk[db] = mfma_bf16(tr_operand(sq + tr_rd, RP, u, db * 64), sb, dk[db]);
-            }
+          for (int db = 0; db < 4; ++db) {
+            dv[db] = mfma_bf16(tr_operand(do_s + tr_rd, RP, u, db * 64), pb, dv[db]);
+            dk[db] = mfma_bf16(tr_operand(q_s + tr_rd, RP, u, db * 64), sb, dk[db]);
           }
         }
-        __syncthreads();
       }
+      if (j + 1 < nseq) store_step(stage ^ 1);
+      __syncthreads();
     }
   }
 
@@ -289,24 +316,40 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BwdParams, int n_c
 // ---------------------------------------------------------------- dQ
 constexpr int QROWS = 128;
 constexpr int KT = 64;
-constexpr int TP = 272;                  // LDS pitch (bytes) of staged K / V rows
-constexpr int TILE_BYTES = KT * TP;
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+constexpr int ROW_BYTES = D * 2;         // staged K / V row: 16 chunks of 16 bytes
+constexpr int TILE_BYTES = KT * ROW_BYTES;
 
-__global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BwdParams, int n_tiles) {
+__global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_tiles, int cap) {
   const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
+  // two stages of K and V tiles, four distinct arrays: the direct-to-LDS loads into
+  // one stage provably never alias the operand reads of the other
+  __shared__ __attribute__((aligned(16))) char lds_k0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_v0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_k1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_v1[TILE_BYTES];
   __shared__ int64_t red[4][4];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
   const int Hkv = p.n_kv_heads, Hq = p.n_q_heads, G = Hq / Hkv, B = p.block_size;
   const int g = blockIdx.x % Hkv;
-  const int tile_id = blockIdx.x / Hkv;
+  const int piece = blockIdx.x / Hkv;
   const int64_t n_q = int64_t(p.n_blocks) * B;
   const int64_t n_rows = n_q * G;
   const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
   const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table);
+
+  // this workgroup's piece: key tiles [j P, j P + P) of row tile tile_id's walk
+  const int32_t* plan = p.dq_plan;
+  const int P = plan[0];
+  if (piece >= plan[1]) return;
+  const int32_t* count = plan + 4;
+  const int32_t* sbase = count + n_tiles;
+  const int32_t* piece_tile = sbase + n_tiles;
+  const int32_t* piece_j = piece_tile + cap;
+  const int tile_id = piece_tile[piece];
+  const int pj = piece_j[piece];
+  const bool split = count[tile_id] > 1;
 
   const int64_t r = int64_t(tile_id) * QROWS + wave * 32 + col;
   const bool row_ok = r < n_rows;
@@ -339,13 +382,27 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BwdParams, int n_til
   const int64_t kstride = int64_t(Hkv) * D;
   const uint32_t row_bytes = uint32_t(kstride * 2);
   const int64_t gofs = int64_t(g) * D;
-  const int ld_row = tid >> 4, ld_ch = tid & 15;
-  const uint32_t ld_off = uint32_t(ld_row) * row_bytes + uint32_t(ld_ch) * 16;
-  const int k_rd = col * TP + half * 16;
-  const int tr_rd = tr_lane_offset(lane, TP);
+  // Direct-to-LDS staging: wave w fills rows 16w .. 16w + 15 of a tile, four rows per
+  // instruction, one 16-byte chunk per lane; slot c of LDS row r holds global chunk
+  // c ^ (r & 15), so the b128 and transpose operand reads below are conflict-free.
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t ld_row_off = uint32_t(16 * wave + (lane >> 4)) * row_bytes;
+  const uint32_t ld_chunk = uint32_t(((lane & 15) ^ (lane >> 4)) * 16);
+  // b128 read of key row col [+32], chunk 2t + half: address (k_rd ^ 32t) [+ 8192]
+  const int k_rd = col * ROW_BYTES + 16 * (half ^ (col & 15));
+  // transpose read (rows 16u + 8hi + 4half + j/4, chunk 4db + c0): (tr_rd[hi] ^ 64db) + 4096u
+  const int tj = lane & 15, tg = lane >> 4;
+  int tr_rd[2];
+#pragma unroll
+  for (int hi2 = 0; hi2 < 2; ++hi2) {
+    const int rr = 8 * hi2 + 4 * half + (tj >> 2);
+    const int c0 = 2 * (tg & 1) + ((tj & 3) >> 1);
+    tr_rd[hi2] = rr * ROW_BYTES + 16 * (c0 ^ rr) + 8 * (tj & 1);
+  }
 
   // phase 0: local context chunks; phase 1: the draft blocks' own keys
-  for (int phase = 0; phase < (p.has_self ? 2 : 1); ++phase) {
+  for (int phase = 0; phase < (p.has_self && pj == 0 ? 2 : 1); ++phase) {
     const bool is_self = phase == 1;
     int64_t lo = 0, hi = 0;
     if (row_ok)
@@ -391,107 +448,138 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BwdParams, int n_til
     }
     if (!(mlo < mhi) || !walk.next()) continue;
     int64_t p0 = walk.seg0;
+    // the context walk of piece pj starts pj * P tiles in; the self walk is one piece
+    int left = is_self ? INT32_MAX : P;
+    if (!is_self) {
+      int64_t skip = int64_t(pj) * P;
+      bool found = true;
+      while (skip > 0) {
+        const int64_t seg_tiles = (walk.seg1 - walk.seg0 + KT - 1) / KT;
+        if (skip < seg_tiles) break;
+        skip -= seg_tiles;
+        if (!walk.next()) {
+          found = false;
+          break;
+        }
+      }
+      if (!found) continue;
+      p0 = walk.seg0 + skip * KT;
+    }
     const uint16_t* kbase = static_cast<const uint16_t*>(is_self ? p.k_self : p.k);
     const uint16_t* vbase = static_cast<const uint16_t*>(is_self ? p.v_self : p.v);
 
-    u32x4 kr[4], vr[4];
     auto tile_of = [&](int64_t pos0, int64_t* l0, int* nvalid) {
       *l0 = walk.local0 + (pos0 - walk.seg0);
       const int64_t n = walk.seg1 - pos0;
       *nvalid = int(n < KT ? n : KT);
     };
-    auto load_tile = [&](int64_t l0, int nvalid) {
+    // the buffers end after the tile's last valid key: rows beyond it read as zero
+    auto dma_tile = [&](int64_t l0, int nvalid, char* kdst, char* vdst) {
       const uint32_t bytes = uint32_t(nvalid - 1) * row_bytes + D * 2;
       const __amdgpu_buffer_rsrc_t kb = make_rsrc(kbase + l0 * kstride + gofs, bytes);
       const __amdgpu_buffer_rsrc_t vb = make_rsrc(vbase + l0 * kstride + gofs, bytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        kr[i] = buffer_load16(kb, ld_off + uint32_t(16 * i) * row_bytes);
-        vr[i] = buffer_load16(vb, ld_off + uint32_t(16 * i) * row_bytes);
+        const uint32_t off = ld_row_off + uint32_t(4 * i) * row_bytes + (ld_chunk ^ uint32_t(64 * i));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kb, (lds_void*)(kdst + (16 * wave_u + 4 * i) * ROW_BYTES), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vb, (lds_void*)(vdst + (16 * wave_u + 4 * i) * ROW_BYTES), 16, off, 0, 0, 0);
       }
     };
-    auto store_tile = [&](int stage) {
-      char* kb = smem + stage * STAGE_BYTES;
-      char* vb = kb + TILE_BYTES;
+    // dS for one staged tile and its contribution dQ^T += K^T dS^T
+    auto compute_tile = [&](const char* kb, const char* vb, int64_t t_p0, int t_n) {
+      f32x16 sv[2], dp[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<u32x4*>(kb + (ld_row + 16 * i) * TP + ld_ch * 16) = kr[i];
-        *reinterpret_cast<u32x4*>(vb + (ld_row + 16 * i) * TP + ld_ch * 16) = vr[i];
+      for (int b2 = 0; b2 < 2; ++b2) {
+        sv[b2] = zero16();
+        dp[b2] = zero16();
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int o = (k_rd ^ (32 * t)) + b2 * 32 * ROW_BYTES;
+          sv[b2] = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kb + o)), qf[t], sv[b2]);
+          dp[b2] = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(vb + o)), dof[t], dp[b2]);
+        }
+      }
+      const bool full = t_n == KT && t_p0 >= lmax && t_p0 + KT <= hmin;
+      int lo_h = -4 * half, lim_h = KT - 4 * half;
+      if (!full) {
+        const int64_t dl = lo - t_p0, dh = hi - t_p0;
+        const int lo_rel = int(dl < -1 ? -1 : (dl > KT ? KT : dl));
+        const int hi_rel = int(dh < -1 ? -1 : (dh > KT ? KT : dh));
+        lo_h = lo_rel - 4 * half;
+        lim_h = (hi_rel < t_n ? hi_rel : t_n) - 4 * half;
+      }
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          // key = kb16 + 4 * half; bounds shifted by the lane's half instead
+          const int kb16 = b2 * 32 + 8 * (v >> 2) + (v & 3);
+          const bool vis = live && kb16 >= lo_h && kb16 < lim_h;
+          const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(sv[b2][v], c2, -lse2)) : 0.f;
+          sv[b2][v] = pv * (dp[b2][v] - dlt);  // dS
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 sb = pack_bf16(sv[u >> 1], u & 1);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(kb + ((tr_rd[0] ^ (64 * db)) + 4096 * u)));
+          const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(kb + ((tr_rd[1] ^ (64 * db)) + 4096 * u)));
+          const bf16x8 a = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          dq[db] = mfma_bf16(a, sb, dq[db]);
+        }
       }
     };
 
     int64_t cur_p0 = p0, cur_l0;
     int cur_n;
     tile_of(cur_p0, &cur_l0, &cur_n);
-    load_tile(cur_l0, cur_n);
-    store_tile(0);
-    __syncthreads();
-    int stage = 0;
-    bool have = true;
-    while (have) {
-      // next tile of the walk
+    dma_tile(cur_l0, cur_n, lds_k0, lds_v0);
+    __syncthreads();  // also waits for the direct-to-LDS loads
+    // One step computes the tile in (kb, vb) while the next tile streams into
+    // (kn, vn); the barrier at its end publishes that tile and retires this one.
+    auto step = [&](const char* kb, const char* vb, char* kn, char* vn) {
       int64_t nxt_p0 = cur_p0 + KT, nxt_l0 = 0;
       int nxt_n = 0;
-      bool have_next = true;
-      if (nxt_p0 >= walk.seg1) {
+      bool have_next = --left > 0;
+      if (have_next && nxt_p0 >= walk.seg1) {
         have_next = walk.next();
         nxt_p0 = have_next ? walk.seg0 : 0;
       }
       if (have_next) {
         tile_of(nxt_p0, &nxt_l0, &nxt_n);
-        load_tile(nxt_l0, nxt_n);
+        dma_tile(nxt_l0, nxt_n, kn, vn);
       }
-
-      const char* kb = smem + stage * STAGE_BYTES;
-      const char* vb = kb + TILE_BYTES;
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        s[b2] = zero16();
-        dp[b2] = zero16();
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int o = k_rd + b2 * 32 * TP + 32 * t;
-          s[b2] = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kb + o)), qf[t], s[b2]);
-          dp[b2] = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(vb + o)), dof[t], dp[b2]);
-        }
-      }
-      const bool full = cur_n == KT && cur_p0 >= lmax && cur_p0 + KT <= hmin;
-      int lo_rel = 0, lim = KT;
-      if (!full) {
-        const int64_t dl = lo - cur_p0, dh = hi - cur_p0;
-        lo_rel = int(dl < -1 ? -1 : (dl > KT ? KT : dl));
-        const int hi_rel = int(dh < -1 ? -1 : (dh > KT ? KT : dh));
-        lim = hi_rel < cur_n ? hi_rel : cur_n;
-      }
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = b2 * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          const bool vis = live && (full || (key >= lo_rel && key < lim));
-          const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[b2][v], c2, -lse2)) : 0.f;
-          s[b2][v] = pv * (dp[b2][v] - dlt);  // dS
-        }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 sb = pack_bf16(s[u >> 1], u & 1);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          dq[db] = mfma_bf16(tr_operand(kb + tr_rd, TP, u, db * 64), sb, dq[db]);
-      }
-
-      if (have_next) store_tile(stage ^ 1);
+      compute_tile(kb, vb, cur_p0, cur_n);
       __syncthreads();
-      stage ^= 1;
       cur_p0 = nxt_p0;
       cur_l0 = nxt_l0;
       cur_n = nxt_n;
-      have = have_next;
+      return have_next;
+    };
+    while (step(lds_k0, lds_v0, lds_k1, lds_v1) && step(lds_k1, lds_v1, lds_k0, lds_v0)) {
     }
   }
 
   if (!row_ok) return;
+  if (split) {
+    // partial sum of piece pj, unscaled, [slot][row in tile][d]
+    float* pp = p.dq_part +
+                ((int64_t(sbase[tile_id] + pj) * Hkv + g) * QROWS + wave * 32 + col) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = db * 32 + 8 * a + 4 * half;
+        *reinterpret_cast<float4*>(pp + d0) = make_float4(dq[db][4 * a], dq[db][4 * a + 1],
+                                                          dq[db][4 * a + 2], dq[db][4 * a + 3]);
+      }
+    return;
+  }
   float* op = p.dq + (qi * Hq + h) * D;
   const float sc = p.scale;
 #pragma unroll
@@ -505,7 +593,156 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BwdParams, int n_til
     }
 }
 
+// ---------------------------------------------------------------- dQ split plan
+// One workgroup.  w_t = key tiles of row tile t's context walk (the kernel's own
+// union of its rows' ranges over all local chunks); P = max(kDqMinPieceTiles,
+// ceil(sum w / target)); count_t = max(1, ceil(w_t / P)) pieces.  Pieces are listed
+// row tile by row tile; split row tiles (count_t > 1) get consecutive partial slots
+// from sbase_t.  Header: P, number of pieces, number of split row tiles.
+constexpr int PLAN_THREADS = 1024;
+
+__global__ __launch_bounds__(PLAN_THREADS) void bwd_dq_plan_kernel(BwdParams, int n_tiles,
+                                                                   int cap, int target) {
+  const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
+  __shared__ int64_t s_w[PLAN_THREADS];
+  __shared__ int s_scan[3][PLAN_THREADS];
+  const int tid = threadIdx.x;
+  const int Hkv = p.n_kv_heads, G = p.n_q_heads / Hkv;
+  const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
+  const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
+  const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table);
+  int32_t* plan = p.dq_plan;
+  int32_t* count = plan + 4;
+  int32_t* sbase = count + n_tiles;
+  int32_t* piece_tile = sbase + n_tiles;
+  int32_t* piece_j = piece_tile + cap;
+  int32_t* multi_tile = piece_j + cap;
+
+  // each thread owns a contiguous run of row tiles
+  const int per = (n_tiles + PLAN_THREADS - 1) / PLAN_THREADS;
+  const int t0 = tid * per < n_tiles ? tid * per : n_tiles;
+  const int t1 = t0 + per < n_tiles ? t0 + per : n_tiles;
+  int64_t wsum = 0;
+  for (int t = t0; t < t1; ++t) {
+    const int64_t r0 = int64_t(t) * QROWS;
+    const int64_t r1 = r0 + QROWS < n_rows ? r0 + QROWS : n_rows;
+    int64_t mlo, mhi;
+    row_span_union(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, G, false, r0, r1, &mlo, &mhi);
+    const int64_t w = walk_tiles(ent, 0, p.n_entries, mlo, mhi, KT);
+    count[t] = int32_t(w < INT32_MAX ? w : INT32_MAX);
+    wsum += w;
+  }
+  s_w[tid] = wsum;
+  __syncthreads();
+  for (int off = PLAN_THREADS / 2; off > 0; off >>= 1) {
+    if (tid < off) s_w[tid] += s_w[tid + off];
+    __syncthreads();
+  }
+  const int64_t W = s_w[0];
+  int64_t P = (W + target - 1) / target;
+  P = P < kDqMinPieceTiles ? kDqMinPieceTiles : P;
+
+  int own[3] = {0, 0, 0};  // pieces, partial slots, split row tiles
+  for (int t = t0; t < t1; ++t) {
+    const int64_t w = count[t];
+    const int c = int(w > P ? (w + P - 1) / P : 1);
+    count[t] = c;
+    own[0] += c;
+    own[1] += c > 1 ? c : 0;
+    own[2] += c > 1 ? 1 : 0;
+  }
+  // exclusive scans of the three per-thread totals
+  for (int k = 0; k < 3; ++k) s_scan[k][tid] = own[k];
+  __syncthreads();
+  for (int off = 1; off < PLAN_THREADS; off <<= 1) {
+    int v[3];
+    for (int k = 0; k < 3; ++k) v[k] = tid >= off ? s_scan[k][tid - off] : 0;
+    __syncthreads();
+    for (int k = 0; k < 3; ++k) s_scan[k][tid] += v[k];
+    __syncthreads();
+  }
+  int at = s_scan[0][tid] - own[0], slot = s_scan[1][tid] - own[1],
+      mi = s_scan[2][tid] - own[2];
+  for (int t = t0; t < t1; ++t) {
+    const int c = count[t];
+    for (int j = 0; j < c; ++j) {
+      piece_tile[at + j] = t;
+      piece_j[at + j] = j;
+    }
+    at += c;
+    if (c > 1) {
+      sbase[t] = slot;
+      slot += c;
+      multi_tile[mi++] = t;
+    } else {
+      sbase[t] = -1;
+    }
+  }
+  if (tid == PLAN_THREADS - 1) {
+    plan[0] = int32_t(P);
+    plan[1] = s_scan[0][tid];
+    plan[2] = s_scan[2][tid];
+    plan[3] = 0;
+  }
+}
+
+// ---------------------------------------------------------------- dQ reduce
+// dQ of a split row tile = scale * sum of its pieces' partials, in piece order.
+__global__ __launch_bounds__(THREADS) void bwd_dq_reduce_kernel(BwdParams, int n_tiles, int cap) {
+  const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
+  const int Hkv = p.n_kv_heads, Hq = p.n_q_heads, G = Hq / Hkv;
+  const int g = blockIdx.x % Hkv;
+  const int m = blockIdx.x / Hkv;
+  const int32_t* plan = p.dq_plan;
+  if (m >= plan[2]) return;
+  const int32_t* count = plan + 4;
+  const int32_t* sbase = count + n_tiles;
+  const int32_t* multi_tile = sbase + n_tiles + 2 * int64_t(cap);
+  const int t = multi_tile[m];
+  const int c = count[t], s0 = sbase[t];
+  const int row = threadIdx.x >> 1, d0 = (threadIdx.x & 1) * 64;
+  const int64_t r = int64_t(t) * QROWS + row;
+  const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
+  if (r >= n_rows) return;
+  float4 acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < c; ++j) {
+    const float* src = p.dq_part + ((int64_t(s0 + j) * Hkv + g) * QROWS + row) * D + d0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 x = *reinterpret_cast<const float4*>(src + 4 * i);
+      acc[i].x += x.x;
+      acc[i].y += x.y;
+      acc[i].z += x.z;
+      acc[i].w += x.w;
+    }
+  }
+  const int64_t qi = r / G;
+  const int h = g * G + int(r % G);
+  float* dst = p.dq + (qi * Hq + h) * D + d0;
+  const float sc = p.scale;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    *reinterpret_cast<float4*>(dst + 4 * i) =
+        make_float4(acc[i].x * sc, acc[i].y * sc, acc[i].z * sc, acc[i].w * sc);
+}
+
 }  // namespace
+
+DqLayout bwd_dq_layout(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
+                       int32_t n_kv_heads) {
+  DqLayout l{};
+  if (n_kv_heads < 1 || n_blocks < 1 || block_size < 1) return l;
+  const int64_t n_rows = int64_t(n_blocks) * block_size * (n_q_heads / n_kv_heads);
+  const int64_t target = (kDqTargetWgs + n_kv_heads - 1) / n_kv_heads;
+  l.n_tiles = (n_rows + QROWS - 1) / QROWS;
+  l.cap = target + l.n_tiles;
+  l.part_slots = 2 * target < l.cap ? 2 * target : l.cap;
+  l.plan_bytes = sizeof(int32_t) * size_t(4 + 3 * l.n_tiles + 2 * l.cap);
+  l.part_bytes = sizeof(float) * size_t(l.part_slots) * n_kv_heads * QROWS * D;
+  return l;
+}
 
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   const int64_t n_q = int64_t(p.n_blocks) * p.block_size;
@@ -528,16 +765,22 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int G = p.n_q_heads / p.n_kv_heads;
-  const int64_t q_tiles = (n_q * G + QROWS - 1) / QROWS;
-  const int64_t q_grid = q_tiles * p.n_kv_heads;
-  if (q_grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (q_grid > 0) {
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(unsigned(q_grid)), dim3(THREADS), 0, stream, p,
-                       int(q_tiles));
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  const DqLayout l = bwd_dq_layout(p.n_blocks, p.block_size, p.n_q_heads, p.n_kv_heads);
+  if (l.n_tiles == 0) return hipSuccess;
+  const int64_t target = (kDqTargetWgs + p.n_kv_heads - 1) / p.n_kv_heads;
+  const int64_t q_grid = l.cap * p.n_kv_heads;
+  if (q_grid > 0x7fffffff || l.cap > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_dq_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, p,
+                     int(l.n_tiles), int(l.cap), int(target));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(unsigned(q_grid)), dim3(THREADS), 0, stream, p,
+                     int(l.n_tiles), int(l.cap));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dq_reduce_kernel, dim3(unsigned(l.n_tiles * p.n_kv_heads)),
+                     dim3(THREADS), 0, stream, p, int(l.n_tiles), int(l.cap));
+  return hipGetLastError();
 }
 
 }  // namespace bsx

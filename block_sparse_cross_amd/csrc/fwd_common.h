@@ -58,6 +58,40 @@ __device__ inline void visible_range(const int64_t* anchor, const int64_t* ctx_b
   *hi = z;
 }
 
+// Union [*mlo, *mhi) of the visible ranges of the query rows [r0, r1) of one KV
+// head (row r is query r / G), per lane (no wave-uniform assumption); empty when no
+// row sees anything (*mlo >= *mhi).
+__device__ inline void row_span_union(const int64_t* anchor, const int64_t* ctx_begin, int64_t S,
+                                      int block_size, int G, bool self_slot, int64_t r0,
+                                      int64_t r1, int64_t* mlo, int64_t* mhi) {
+  *mlo = INT64_MAX;
+  *mhi = INT64_MIN;
+  const int64_t b0 = r0 / G / block_size, b1 = (r1 - 1) / G / block_size;
+  for (int64_t b = b0; b <= b1; ++b) {
+    int64_t lo, hi;
+    visible_range(anchor, ctx_begin, S, block_size, self_slot, b, &lo, &hi);
+    if (lo < hi) {
+      *mlo = lo < *mlo ? lo : *mlo;
+      *mhi = hi > *mhi ? hi : *mhi;
+    }
+  }
+}
+
+// Key tiles of `key_tile` positions a walk over entries [e0, e1) cut to [mlo, mhi)
+// visits (each segment is tiled from its first position), per lane.
+__device__ inline int64_t walk_tiles(const ChunkEntry* ent, int e0, int e1, int64_t mlo,
+                                     int64_t mhi, int key_tile) {
+  int64_t tiles = 0;
+  if (!(mlo < mhi)) return 0;
+  for (int e = e0; e < e1; ++e) {
+    const int64_t a = ent[e].start > mlo ? ent[e].start : mlo;
+    const int64_t end = ent[e].start + int64_t(ent[e].len);
+    const int64_t z = end < mhi ? end : mhi;
+    if (a < z) tiles += (z - a + key_tile - 1) / key_tile;
+  }
+  return tiles;
+}
+
 // Walks the key segments a workgroup must visit for one slot: each segment is a
 // run of positions [seg0, seg1) stored at local rows local0 .. local0 + (seg1 - seg0),
 // already cut to the union [minlo, maxhi) of the ranges its rows can see.

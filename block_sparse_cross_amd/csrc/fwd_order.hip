@@ -46,29 +46,12 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
     const bool is_self = p.has_self && slot == p.n_slots;
     const int64_t r0 = int64_t(tile) * kFwdRows;
     const int64_t r1 = r0 + kFwdRows < n_rows ? r0 + kFwdRows : n_rows;
-    const int64_t b0 = r0 / G / p.block_size, b1 = (r1 - 1) / G / p.block_size;
-    int64_t mlo = INT64_MAX, mhi = INT64_MIN;
-    for (int64_t b = b0; b <= b1; ++b) {
-      int64_t lo, hi;
-      visible_range(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, is_self, b, &lo, &hi);
-      if (lo < hi) {
-        mlo = lo < mlo ? lo : mlo;
-        mhi = hi > mhi ? hi : mhi;
-      }
-    }
+    int64_t mlo, mhi;
+    row_span_union(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, G, is_self, r0, r1, &mlo, &mhi);
     int64_t tiles = 0;
-    if (mlo < mhi) {
-      if (is_self) {
-        tiles = (mhi - mlo + kFwdKeyTile - 1) / kFwdKeyTile;
-      } else {
-        for (int e = slot_ptr[slot]; e < slot_ptr[slot + 1]; ++e) {
-          const int64_t a = ent[e].start > mlo ? ent[e].start : mlo;
-          const int64_t end = ent[e].start + int64_t(ent[e].len);
-          const int64_t z = end < mhi ? end : mhi;
-          if (a < z) tiles += (z - a + kFwdKeyTile - 1) / kFwdKeyTile;
-        }
-      }
-    }
+    if (mlo < mhi)
+      tiles = is_self ? (mhi - mlo + kFwdKeyTile - 1) / kFwdKeyTile
+                      : walk_tiles(ent, slot_ptr[slot], slot_ptr[slot + 1], mlo, mhi, kFwdKeyTile);
     work[it] = uint16_t(tiles < 0xffff ? tiles : 0xffff);
   }
   for (int i = tid; i < kXcds * kKeys; i += kThreads) (&pos[0][0])[i] = 0;
