@@ -600,12 +600,17 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
 // row tile by row tile; split row tiles (count_t > 1) get consecutive partial slots
 // from sbase_t.  Header: P, number of pieces, number of split row tiles.
 constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_LDS_TILES = 2048;    // plans up to this many row tiles ...
+constexpr int PLAN_LDS_ENTRIES = 2048;  // ... and chunks work from LDS
 
 __global__ __launch_bounds__(PLAN_THREADS) void bwd_dq_plan_kernel(BwdParams, int n_tiles,
                                                                    int cap, int target) {
   const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
   __shared__ int64_t s_w[PLAN_THREADS];
   __shared__ int s_scan[3][PLAN_THREADS];
+  __shared__ __attribute__((aligned(16))) ChunkEntry s_ent[PLAN_LDS_ENTRIES];
+  __shared__ int64_t s_lo[PLAN_LDS_TILES], s_hi[PLAN_LDS_TILES];
+  __shared__ int32_t s_tiles[PLAN_LDS_TILES];
   const int tid = threadIdx.x;
   const int Hkv = p.n_kv_heads, G = p.n_q_heads / Hkv;
   const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
@@ -622,15 +627,39 @@ __global__ __launch_bounds__(PLAN_THREADS) void bwd_dq_plan_kernel(BwdParams, in
   const int per = (n_tiles + PLAN_THREADS - 1) / PLAN_THREADS;
   const int t0 = tid * per < n_tiles ? tid * per : n_tiles;
   const int t1 = t0 + per < n_tiles ? t0 + per : n_tiles;
-  int64_t wsum = 0;
-  for (int t = t0; t < t1; ++t) {
+  auto span = [&](int t, int64_t* mlo, int64_t* mhi) {
     const int64_t r0 = int64_t(t) * QROWS;
     const int64_t r1 = r0 + QROWS < n_rows ? r0 + QROWS : n_rows;
-    int64_t mlo, mhi;
-    row_span_union(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, G, false, r0, r1, &mlo, &mhi);
-    const int64_t w = walk_tiles(ent, 0, p.n_entries, mlo, mhi, KT);
-    count[t] = int32_t(w < INT32_MAX ? w : INT32_MAX);
-    wsum += w;
+    row_span_union(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, G, false, r0, r1, mlo, mhi);
+  };
+  int64_t wsum = 0;
+  if (n_tiles <= PLAN_LDS_TILES && p.n_entries <= PLAN_LDS_ENTRIES) {
+    // small plan: ranges and entries in LDS, (row tile, entry) pairs spread over all lanes
+    for (int e = tid; e < p.n_entries; e += PLAN_THREADS) s_ent[e] = ent[e];
+    for (int t = tid; t < n_tiles; t += PLAN_THREADS) {
+      span(t, &s_lo[t], &s_hi[t]);
+      s_tiles[t] = 0;
+    }
+    __syncthreads();
+    const int64_t n_pairs = int64_t(n_tiles) * p.n_entries;
+    for (int64_t i = tid; i < n_pairs; i += PLAN_THREADS) {
+      const int t = int(i / p.n_entries), e = int(i % p.n_entries);
+      const int64_t w = walk_tiles(s_ent, e, e + 1, s_lo[t], s_hi[t], KT);
+      if (w) atomicAdd(&s_tiles[t], int(w));
+    }
+    __syncthreads();
+    for (int t = t0; t < t1; ++t) {
+      count[t] = s_tiles[t];
+      wsum += s_tiles[t];
+    }
+  } else {
+    for (int t = t0; t < t1; ++t) {
+      int64_t mlo, mhi;
+      span(t, &mlo, &mhi);
+      const int64_t w = walk_tiles(ent, 0, p.n_entries, mlo, mhi, KT);
+      count[t] = int32_t(w < INT32_MAX ? w : INT32_MAX);
+      wsum += w;
+    }
   }
   s_w[tid] = wsum;
   __syncthreads();
@@ -688,11 +717,16 @@ __global__ __launch_bounds__(PLAN_THREADS) void bwd_dq_plan_kernel(BwdParams, in
 
 // ---------------------------------------------------------------- dQ reduce
 // dQ of a split row tile = scale * sum of its pieces' partials, in piece order.
+// One workgroup per (split row tile, KV head, 32-row group); partials are read once.
+constexpr int RED_ROWS = 32;
+
 __global__ __launch_bounds__(THREADS) void bwd_dq_reduce_kernel(BwdParams, int n_tiles, int cap) {
   const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
   const int Hkv = p.n_kv_heads, Hq = p.n_q_heads, G = Hq / Hkv;
+  constexpr int kGroups = QROWS / RED_ROWS;
   const int g = blockIdx.x % Hkv;
-  const int m = blockIdx.x / Hkv;
+  const int rg = (blockIdx.x / Hkv) % kGroups;
+  const int m = blockIdx.x / (Hkv * kGroups);
   const int32_t* plan = p.dq_plan;
   if (m >= plan[2]) return;
   const int32_t* count = plan + 4;
@@ -700,30 +734,26 @@ __global__ __launch_bounds__(THREADS) void bwd_dq_reduce_kernel(BwdParams, int n
   const int32_t* multi_tile = sbase + n_tiles + 2 * int64_t(cap);
   const int t = multi_tile[m];
   const int c = count[t], s0 = sbase[t];
-  const int row = threadIdx.x >> 1, d0 = (threadIdx.x & 1) * 64;
+  const int row = rg * RED_ROWS + (threadIdx.x >> 3), d0 = (threadIdx.x & 7) * 16;
   const int64_t r = int64_t(t) * QROWS + row;
   const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
   if (r >= n_rows) return;
-  float4 acc[16];
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  f32x4v acc[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < c; ++j) {
     const float* src = p.dq_part + ((int64_t(s0 + j) * Hkv + g) * QROWS + row) * D + d0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float4 x = *reinterpret_cast<const float4*>(src + 4 * i);
-      acc[i].x += x.x;
-      acc[i].y += x.y;
-      acc[i].z += x.z;
-      acc[i].w += x.w;
-    }
+    for (int i = 0; i < 4; ++i)
+      acc[i] += __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(src) + i);
   }
   const int64_t qi = r / G;
   const int h = g * G + int(r % G);
   float* dst = p.dq + (qi * Hq + h) * D + d0;
   const float sc = p.scale;
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < 4; ++i)
     *reinterpret_cast<float4*>(dst + 4 * i) =
         make_float4(acc[i].x * sc, acc[i].y * sc, acc[i].z * sc, acc[i].w * sc);
 }
@@ -778,8 +808,9 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
                      int(l.n_tiles), int(l.cap));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_reduce_kernel, dim3(unsigned(l.n_tiles * p.n_kv_heads)),
-                     dim3(THREADS), 0, stream, p, int(l.n_tiles), int(l.cap));
+  hipLaunchKernelGGL(bwd_dq_reduce_kernel,
+                     dim3(unsigned(l.n_tiles * p.n_kv_heads * (QROWS / RED_ROWS))), dim3(THREADS),
+                     0, stream, p, int(l.n_tiles), int(l.cap));
   return hipGetLastError();
 }
 

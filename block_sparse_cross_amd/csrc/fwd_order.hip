@@ -11,8 +11,8 @@
 // XCD's L2).  The order changes no result, only the schedule.
 //
 // One workgroup of 1024 threads: per-(row tile, slot) tile counts go to LDS, then a
-// counting sort on the clamped count per XCD (LDS histogram, suffix sums, scatter
-// with LDS atomics; items of equal count keep no particular order).
+// counting sort on the clamped count per XCD (one LDS histogram per wave, so atomics
+// meet only within a wave; suffix sums; scatter; equal counts keep no particular order).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -24,18 +24,30 @@ namespace bsx {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kKeys = 256;  // sort key: 0 = no item, else 1 + min(tiles, 254)
+constexpr int kKeys = 64;   // sort key: 0 = no item, else 1 + min(tiles, 62)
+constexpr int kWaves = kThreads / 64;
+constexpr int kTableLdsWords = 4096;  // chunk tables up to 16 KiB are read from LDS
 
 __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t* order,
                                                              int n_tiles, int n_pairs) {
   const BSX_KARG FwdParams& p = kernel_arg0<FwdParams>();
   __shared__ uint16_t work[kOrderMaxItems];
-  __shared__ int32_t pos[kXcds][kKeys];
+  __shared__ int32_t pos[kXcds][kKeys][kWaves];
   const int tid = threadIdx.x;
   const int n_out = p.n_slots + p.has_self;
   const int G = p.n_q_heads / p.n_kv_heads;
   const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
+  __shared__ __attribute__((aligned(16))) uint32_t s_table[kTableLdsWords];
+  // the chunk table, copied to LDS when it fits: every lane walks it below
   const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
+  const int64_t table_bytes =
+      p.entries_off + int64_t(reinterpret_cast<const int32_t*>(table)[p.n_slots]) * 16;
+  if (table_bytes <= int64_t(sizeof(s_table))) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(table);
+    for (int i = tid; i < int(table_bytes / 4); i += kThreads) s_table[i] = src[i];
+    __syncthreads();
+    table = reinterpret_cast<const char*>(s_table);
+  }
   const int32_t* slot_ptr = reinterpret_cast<const int32_t*>(table);
   const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table + p.entries_off);
 
@@ -54,17 +66,15 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
                       : walk_tiles(ent, slot_ptr[slot], slot_ptr[slot + 1], mlo, mhi, kFwdKeyTile);
     work[it] = uint16_t(tiles < 0xffff ? tiles : 0xffff);
   }
-  for (int i = tid; i < kXcds * kKeys; i += kThreads) (&pos[0][0])[i] = 0;
   __syncthreads();
 
   // ---- workgroup slot bid holds, in the natural order, item (pair, tile) below
   const int per_xcd = (n_pairs + kXcds - 1) / kXcds;
-  const int64_t n_bids = int64_t(kXcds) * per_xcd * n_tiles;
-  auto key_of = [&](int64_t bid, int* code) {
-    const int xcd = int(bid % kXcds);
-    const int64_t j = bid / kXcds;
-    const int pair = int(j / n_tiles) * kXcds + xcd;
-    const int tile = n_tiles - 1 - int(j % n_tiles);
+  const int n_bids = kXcds * per_xcd * n_tiles;
+  auto key_of = [&](int bid, int* code) {
+    const int xcd = bid % kXcds, j = bid / kXcds;
+    const int pair = (j / n_tiles) * kXcds + xcd;
+    const int tile = n_tiles - 1 - j % n_tiles;
     if (pair >= n_pairs) {
       *code = -1;
       return 0;
@@ -73,44 +83,41 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
     const int w = work[tile * n_out + pair / p.n_kv_heads];
     return 1 + (w < kKeys - 2 ? w : kKeys - 2);
   };
-  for (int64_t bid = tid; bid < n_bids; bid += kThreads) {
+  static_assert(kKeys == 64, "one key per lane in the prefix pass");
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < kXcds * kKeys * kWaves; i += kThreads) (&pos[0][0][0])[i] = 0;
+  __syncthreads();
+  for (int bid = tid; bid < n_bids; bid += kThreads) {
     int code;
     const int key = key_of(bid, &code);
-    atomicAdd(&pos[bid % kXcds][key], 1);
+    atomicAdd(&pos[bid % kXcds][key][wave], 1);
   }
   __syncthreads();
-
-  // ---- start of each key's run: items with larger keys come first (suffix sums).
-  // One wave per XCD; lane l owns keys 255 - 4l .. 252 - 4l.
-  static_assert(kKeys == 4 * 64, "one wave of 64 lanes, four keys each");
-  if (tid < kXcds * 64) {
-    const int x = tid >> 6, l = tid & 63;
-    int c[4], own = 0;
+  if (wave < kXcds) {
+    const int x = wave, key = kKeys - 1 - lane;
+    int own = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      c[q] = pos[x][kKeys - 1 - (4 * l + q)];
-      own += c[q];
-    }
+    for (int w = 0; w < kWaves; ++w) own += pos[x][key][w];
     int incl = own;
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(incl, off);
-      if (l >= off) incl += y;
+      if (lane >= off) incl += y;
     }
     int acc = incl - own;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      pos[x][kKeys - 1 - (4 * l + q)] = acc;
-      acc += c[q];
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = pos[x][key][w];
+      pos[x][key][w] = acc;
+      acc += c;
     }
   }
   __syncthreads();
-
-  for (int64_t bid = tid; bid < n_bids; bid += kThreads) {
+  for (int bid = tid; bid < n_bids; bid += kThreads) {
     int code;
     const int key = key_of(bid, &code);
-    const int x = int(bid % kXcds);
-    const int at = atomicAdd(&pos[x][key], 1);
-    order[int64_t(at) * kXcds + x] = code;
+    const int x = bid % kXcds;
+    const int at = atomicAdd(&pos[x][key][wave], 1);
+    order[at * kXcds + x] = code;
   }
 }
 
@@ -123,6 +130,7 @@ hipError_t launch_fwd_order(const FwdParams& p, int32_t* order, hipStream_t stre
   const int64_t n_out = int64_t(p.n_slots) + p.has_self;
   if (n_tiles * n_out > kOrderMaxItems) return hipErrorInvalidValue;
   const int64_t n_pairs = int64_t(p.n_kv_heads) * n_out;
+  if (kXcds * ((n_pairs + kXcds - 1) / kXcds) * n_tiles > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fwd_order_kernel, dim3(1), dim3(kThreads), 0, stream, p, order,
                      int(n_tiles), int(n_pairs));
   return hipGetLastError();
