@@ -280,9 +280,11 @@ def cpu_baseline(wl, plan0, seconds: float):
                       f"workload, {dt:.1f} s"}
 
 
-# Sources of the forward kernel; the recorded HBM traffic is valid only for them.
+# Sources of the forward kernel; the recorded HBM traffic is valid only for them (of the
+# shared internal header, only the declarations the forward kernel reads).
 FWD_SOURCES = ["block_sparse_cross_amd/csrc/fwd_bf16.hip", "block_sparse_cross_amd/csrc/fwd_common.h",
-               "block_sparse_cross_amd/csrc/mfma_common.h", "block_sparse_cross_amd/csrc/bsx_internal.h"]
+               "block_sparse_cross_amd/csrc/mfma_common.h"]
+FWD_HEADER = "block_sparse_cross_amd/csrc/bsx_internal.h"
 
 
 def fwd_sources_sha256() -> str:
@@ -291,6 +293,9 @@ def fwd_sources_sha256() -> str:
     for rel in FWD_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(ROOT, FWD_HEADER), "rb") as f:
+        text = f.read()
+    h.update(text[text.index(b"struct ChunkEntry"):text.index(b"struct BwdParams")])
     return h.hexdigest()
 
 
