@@ -45,6 +45,8 @@ def parse():
                     help="time budget of the oracle's CPU baseline sample (0 skips it)")
     ap.add_argument("--fwd-reps", type=int, default=50,
                     help="event-timed launches of the forward kernel for the roofline")
+    ap.add_argument("--planners", action="store_true",
+                    help="print the chunk-placement comparison (imbalance, host us) and exit")
     ap.add_argument("--no-merge-bench", action="store_true",
                     help="skip the standalone 64-set merge measurement")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -315,6 +317,38 @@ def recorded_traffic(workload: str):
     return None
 
 
+def planner_comparison(device, reps: int = 200):
+    """Chunk placements on the planned workloads' realized costs (cost kernel on the GPU):
+    imbalance and host time per plan for LPT and the static layouts the pages compare."""
+    import torch
+
+    import block_sparse_cross_amd as bsx
+    from workloads import get_config, make_workload
+
+    out = {}
+    for name in ("b27_s64k", "rank_p64_s1m", "train_pack128k"):
+        cfg = get_config(name)
+        wl = make_workload(cfg)
+        shape = bsx.Shape(wl.n_blocks, cfg.block_size, cfg.n_q_heads, cfg.n_kv_heads, cfg.ctx_len)
+        an = torch.from_numpy(wl.anchor).to(device)
+        be = torch.from_numpy(wl.ctx_begin).to(device)
+        _, cost, _ = bsx.cost(shape, an, be, bsx.Chunks(wl.chunk_start, wl.chunk_len),
+                              with_counts=False)
+        cost = cost.cpu().numpy()
+        res = {"n_chunks": int(cost.shape[0]), "n_bins": cfg.n_bins}
+        for mode in ("lpt", "zigzag", "round_robin", "contiguous"):
+            r = bsx.place(mode, cost, cfg.n_bins)
+            ts = []
+            for _ in range(reps):
+                t0 = time.perf_counter_ns()
+                bsx.place(mode, cost, cfg.n_bins)
+                ts.append(time.perf_counter_ns() - t0)
+            res[mode] = {"imbalance": round(r.imbalance, 5),
+                         "host_us": round(float(np.median(ts)) / 1e3, 2)}
+        out[name] = res
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -330,6 +364,11 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.planners:
+        print(json.dumps({"planners": planner_comparison(dev),
+                          "note": "host_us: median per call through the Python binding"}),
+              flush=True)
+        return
     if args.calibrate_copy_mib > 0:
         # a plain elementwise kernel of known traffic (reads and writes N MiB with
         # ordinary loads and stores), the reference for the HBM byte counters

@@ -11,6 +11,6 @@ this package only marshals torch tensors (device memory, current stream) into it
 """
 from .api import (BsxError, Chunks, LptResult, Prepared, Shape, abi_version, attn_bwd,  # noqa: F401
                   attn_fwd, bwd_workspace_bytes, cost, cost_workspace_bytes,
-                  fwd_workspace_bytes, lpt, lse_merge, prepare_attn_bwd, prepare_attn_fwd,
+                  fwd_workspace_bytes, lpt, lse_merge, place, prepare_attn_bwd, prepare_attn_fwd,
                   prepare_cost, prepare_lse_merge, validate_mask)
 from ._lib import lib as load_library  # noqa: F401

@@ -57,6 +57,8 @@ _SIGNATURES = [
                          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     ("bsx_lpt", c_int, [c_int32, POINTER(c_int64), c_int32, POINTER(c_int32), POINTER(c_int64),
                         POINTER(c_int64), POINTER(c_double)]),
+    ("bsx_place", c_int, [c_int32, c_int32, POINTER(c_int64), c_int32, POINTER(c_int32),
+                          POINTER(c_int64), POINTER(c_int64), POINTER(c_double)]),
     ("bsx_fwd_workspace", c_size_t, [POINTER(BsxShape), POINTER(BsxChunks)]),
     ("bsx_attn_fwd", c_int, [POINTER(BsxShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_void_p, POINTER(BsxChunks), c_void_p, c_void_p,

@@ -143,6 +143,24 @@ def lpt(cost, n_bins: int) -> LptResult:
     return LptResult(bin_of, loads, int(ms.value), float(imb.value))
 
 
+PLACEMENTS = {"lpt": 0, "contiguous": 1, "zigzag": 2, "round_robin": 3}
+
+
+def place(mode: str, cost, n_bins: int) -> LptResult:
+    """Chunk placement by a named rule (bsx_place): lpt, contiguous, zigzag, round_robin."""
+    c = np.ascontiguousarray(cost, dtype=np.int64)
+    n = int(c.shape[0])
+    bin_of = np.empty(n, np.int32)
+    loads = np.empty(max(int(n_bins), 0), np.int64)
+    ms = ctypes.c_int64(0)
+    imb = ctypes.c_double(0.0)
+    check(lib().bsx_place(PLACEMENTS[mode], n, c.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                          int(n_bins), bin_of.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                          loads.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ctypes.byref(ms),
+                          ctypes.byref(imb)))
+    return LptResult(bin_of, loads, int(ms.value), float(imb.value))
+
+
 def cost_workspace_bytes(n_chunks: int) -> int:
     return int(lib().bsx_cost_workspace(int(n_chunks)))
 

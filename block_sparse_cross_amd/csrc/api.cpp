@@ -10,6 +10,7 @@
 #include <cstring>
 #include <limits>
 #include <numeric>
+#include <queue>
 #include <string>
 #include <vector>
 
@@ -241,13 +242,53 @@ bsx_status bsx_lpt(int32_t n_items, const int64_t* cost, int32_t n_bins, int32_t
     return cost[a] != cost[b] ? cost[a] > cost[b] : a < b;
   });
   std::vector<int64_t> load(n_bins, 0);
+  // least loaded bin first, ties to the lower index: a min-heap on (load, index)
+  typedef std::pair<int64_t, int32_t> Bin;
+  std::priority_queue<Bin, std::vector<Bin>, std::greater<Bin>> heap;
+  for (int32_t j = 0; j < n_bins; ++j) heap.push(Bin(0, j));
   int64_t total = 0;
   for (int32_t i : order) {
-    int32_t best = 0;
-    for (int32_t j = 1; j < n_bins; ++j)
-      if (load[j] < load[best]) best = j;  // strict: ties keep the lower index
+    const int32_t best = heap.top().second;
+    heap.pop();
     bin_of[i] = best;
     load[best] += cost[i];
+    total += cost[i];
+    heap.push(Bin(load[best], best));
+  }
+  const int64_t ms = *std::max_element(load.begin(), load.end());
+  if (bin_load) std::copy(load.begin(), load.end(), bin_load);
+  if (makespan) *makespan = ms;
+  if (imbalance)
+    *imbalance = total > 0 ? double(ms) / (double(total) / double(n_bins)) - 1.0 : 0.0;
+  return ok();
+}
+
+bsx_status bsx_place(int32_t mode, int32_t n_items, const int64_t* cost, int32_t n_bins,
+                     int32_t* bin_of, int64_t* bin_load, int64_t* makespan, double* imbalance) {
+  if (mode == BSX_PLACE_LPT)
+    return bsx_lpt(n_items, cost, n_bins, bin_of, bin_load, makespan, imbalance);
+  if (mode != BSX_PLACE_CONTIGUOUS && mode != BSX_PLACE_ZIGZAG && mode != BSX_PLACE_ROUND_ROBIN)
+    return fail(BSX_E_INVALID, "placement mode %d is not one of 0..3", mode);
+  if (n_items < 0) return fail(BSX_E_INVALID, "n_items = %d < 0", n_items);
+  if (n_bins < 1) return fail(BSX_E_INVALID, "n_bins = %d < 1", n_bins);
+  if (n_items > 0 && (!cost || !bin_of)) return fail(BSX_E_INVALID, "cost/bin_of is NULL");
+  for (int32_t i = 0; i < n_items; ++i)
+    if (cost[i] < 0) return fail(BSX_E_INVALID, "cost[%d] = %lld < 0", i, (long long)cost[i]);
+  const int64_t n = n_items, P = n_bins;
+  std::vector<int64_t> load(size_t(n_bins), 0);
+  int64_t total = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t b;
+    if (mode == BSX_PLACE_CONTIGUOUS) {
+      b = i * P / n;
+    } else if (mode == BSX_PLACE_ZIGZAG) {
+      const int64_t run = i * 2 * P / n;
+      b = run < P ? run : 2 * P - 1 - run;
+    } else {
+      b = i % P;
+    }
+    bin_of[i] = int32_t(b);
+    load[size_t(b)] += cost[i];
     total += cost[i];
   }
   const int64_t ms = *std::max_element(load.begin(), load.end());

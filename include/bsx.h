@@ -141,6 +141,29 @@ bsx_status bsx_lpt(int32_t n_items, const int64_t* cost, int32_t n_bins, int32_t
                    int64_t* bin_load, int64_t* makespan, double* imbalance);
 
 /* ---------------------------------------------------------------------------
+ * Host: chunk placement by a named rule, for comparing balancing strategies.
+ * Split-KV page, Figures & tables (CP comparison table, load-balancing column):
+ * Split-KV balances chunks by cost-aware LPT, Ring Attention by zigzag, RingX not
+ * at all.  Items are chunks in context order, i = 0 .. n_items - 1, P = n_bins:
+ *   BSX_PLACE_LPT          as bsx_lpt
+ *   BSX_PLACE_CONTIGUOUS   bin = floor(i * P / n_items): P runs of consecutive chunks
+ *   BSX_PLACE_ZIGZAG       s = floor(i * 2P / n_items) (2P runs); bin = s if s < P,
+ *                          else 2P - 1 - s: bin r holds runs r and 2P - 1 - r
+ *   BSX_PLACE_ROUND_ROBIN  bin = i mod P
+ * Only LPT reads the costs to place; every rule reports loads, makespan and
+ * imbalance the same way as bsx_lpt.  Arguments as bsx_lpt.
+ */
+typedef enum {
+  BSX_PLACE_LPT = 0,
+  BSX_PLACE_CONTIGUOUS = 1,
+  BSX_PLACE_ZIGZAG = 2,
+  BSX_PLACE_ROUND_ROBIN = 3
+} bsx_placement;
+
+bsx_status bsx_place(int32_t mode, int32_t n_items, const int64_t* cost, int32_t n_bins,
+                     int32_t* bin_of, int64_t* bin_load, int64_t* makespan, double* imbalance);
+
+/* ---------------------------------------------------------------------------
  * Device: forward partials.  For every query row (q, h) and output slot s:
  * the partial (O, LSE) over the visible keys of the chunks mapped to s; with
  * k_self/v_self given, one more slot (index n_slots, last) over the block's own

@@ -28,4 +28,5 @@ from .attention import (  # noqa: F401
 from .merge import lse_merge  # noqa: F401
 from .cost import chunk_costs  # noqa: F401
 from .lpt import lpt, lpt_makespan_opt  # noqa: F401
+from .placement import contiguous, zigzag, round_robin  # noqa: F401
 from .backward import attention_backward  # noqa: F401

@@ -165,3 +165,39 @@ def test_python_binding_checks_buffer_shapes_on_cpu_tensors():
     q = torch.zeros((16, 8, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         bsx.attn_fwd(shape, q, q, q, None, None, None, None, ch)
+
+
+@pytest.mark.parametrize("mode", ["contiguous", "zigzag", "round_robin", "lpt"])
+@pytest.mark.parametrize("seed", range(4))
+def test_place_matches_oracle_random(mode, seed):
+    rng = np.random.default_rng(100 + seed)
+    n, P = int(rng.integers(1, 400)), int(rng.integers(1, 80))
+    cost = rng.integers(0, 10**12, n)
+    got = bsx.place(mode, cost, P)
+    fn = {"contiguous": oracle.contiguous, "zigzag": oracle.zigzag,
+          "round_robin": oracle.round_robin, "lpt": oracle.lpt}[mode]
+    b, loads, ms, imb = fn(cost.tolist(), P)
+    assert got.bin_of.tolist() == list(b)
+    assert got.loads.tolist() == list(loads) and got.makespan == ms
+    assert got.imbalance == pytest.approx(imb, rel=1e-12, abs=1e-15)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_place_matches_oracle_on_workload_costs(idx):
+    wl = make_workload(CONFIGS[idx])
+    _, cost = oracle.chunk_costs(wl.anchor, wl.ctx_begin, wl.cfg.block_size, wl.chunk_start,
+                                 wl.chunk_len)
+    for mode, fn in [("contiguous", oracle.contiguous), ("zigzag", oracle.zigzag),
+                     ("round_robin", oracle.round_robin)]:
+        got = bsx.place(mode, cost, wl.cfg.n_bins)
+        b, loads, ms, _ = fn(cost.tolist(), wl.cfg.n_bins)
+        assert got.bin_of.tolist() == list(b) and got.makespan == ms
+
+
+def test_place_rejects_bad_mode_and_arguments():
+    L = bsx.load_library()
+    assert L.bsx_place(7, 0, None, 1, None, None, None, None) == BSX_E_INVALID
+    with pytest.raises(bsx.BsxError):
+        bsx.place("zigzag", [1, 2], 0)
+    with pytest.raises(bsx.BsxError):
+        bsx.place("round_robin", [1, -1], 2)
