@@ -45,6 +45,8 @@ def parse():
                     help="time budget of the oracle's CPU baseline sample (0 skips it)")
     ap.add_argument("--fwd-reps", type=int, default=50,
                     help="event-timed launches of the forward kernel for the roofline")
+    ap.add_argument("--sweep", action="store_true",
+                    help="print the fixed-query-budget context sweep (S = 16K .. 1M) and exit")
     ap.add_argument("--planners", action="store_true",
                     help="print the chunk-placement comparison (imbalance, host us) and exit")
     ap.add_argument("--no-merge-bench", action="store_true",
@@ -78,7 +80,7 @@ def rank_fwd_flops(wl, local_chunks) -> float:
 class Step:
     """Device-resident inputs, preallocated outputs and workspaces, and one-step runner."""
 
-    def __init__(self, wl, device):
+    def __init__(self, wl, device, device_kv: bool = False):
         import torch
 
         import block_sparse_cross_amd as bsx
@@ -102,8 +104,18 @@ class Step:
         # plan once to learn which chunks are local (deterministic: every step replans the same)
         self.plan0 = make_plan(self.shape, wl.chunk_start, wl.chunk_len, c.slot_mode, c.n_bins,
                                self.anchor, self.begin, self.cost_ws, self.cost_out)
-        k, v = wl.kv_chunks(self.plan0.local_chunks)
-        self.q, self.k, self.v = up(wl.q), up(k), up(v)
+        if device_kv:
+            # timing only: context K/V drawn on the device (seeded), not on the host
+            n_loc = int(np.sum(wl.chunk_len[self.plan0.local_chunks]))
+            g = torch.Generator(device=device)
+            g.manual_seed(c.seed)
+            kv_shape = (n_loc, c.n_kv_heads, c.head_dim)
+            self.k = (torch.randn(kv_shape, generator=g, device=device) * c.sigma).to(dt)
+            self.v = (torch.randn(kv_shape, generator=g, device=device) * c.sigma).to(dt)
+            self.q = up(wl.q)
+        else:
+            k, v = wl.kv_chunks(self.plan0.local_chunks)
+            self.q, self.k, self.v = up(wl.q), up(k), up(v)
         self.ks = up(wl.k_self) if c.self_slot else None
         self.vs = up(wl.v_self) if c.self_slot else None
         ch = self.plan0.chunks
@@ -317,6 +329,38 @@ def recorded_traffic(workload: str):
     return None
 
 
+def context_sweep(device, steps: int = 20, warmup: int = 3):
+    """Fixed query budget (512 draft queries), context S = 16K .. 1M: useful TFLOP/s of the
+    step and of the forward launch, per S."""
+    import torch
+
+    from workloads import SWEEP_CTX, make_workload, sweep_config
+
+    rows = []
+    for S in SWEEP_CTX:
+        wl = make_workload(sweep_config(S))
+        st = Step(wl, device, device_kv=True)
+        st.prepare()
+        for _ in range(warmup):
+            st.run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            st.run()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        fwd_s = time_forward(st, 10)
+        rows.append({"ctx_len": S, "n_queries": wl.n_queries, "ms_per_step": round(dt * 1e3, 4),
+                     "step_tflops": round(st.step_flops / dt / 1e12, 2),
+                     "fwd_us": round(fwd_s * 1e6, 2),
+                     "fwd_tflops": round(st.fwd_flops / fwd_s / 1e12, 2),
+                     "lpt_imbalance": round(st.plan0.imbalance, 5)})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        del st
+        torch.cuda.empty_cache()
+    return rows
+
+
 def planner_comparison(device, reps: int = 200):
     """Chunk placements on the planned workloads' realized costs (cost kernel on the GPU):
     imbalance and host time per plan for LPT and the static layouts the pages compare."""
@@ -364,6 +408,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        print(json.dumps({"sweep": context_sweep(dev)}), flush=True)
+        return
     if args.planners:
         print(json.dumps({"planners": planner_comparison(dev),
                           "note": "host_us: median per call through the Python binding"}),
@@ -381,7 +428,8 @@ def main():
         del src, dst
     cfg = get_config(args.workload)
     wl = make_workload(cfg, args.seed)
-    step = Step(wl, dev)
+    # sweep workloads draw their (large) context K/V on the device: timing only
+    step = Step(wl, dev, device_kv=cfg.name.startswith("sweep_"))
     step.prepare()
     print(f"# workload {cfg.name}: blocks={wl.n_blocks} queries={wl.n_queries} "
           f"local_chunks={len(step.plan0.local_chunks)} fwd useful GFLOP={step.fwd_flops / 1e9:.2f}",

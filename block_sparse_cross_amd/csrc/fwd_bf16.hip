@@ -92,22 +92,27 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
   const int wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
 
-  // Workgroup i runs on XCD i % 8.  All row tiles of one (KV head, slot) pair go to
-  // the same XCD (pair p -> XCD p % 8) so they share that XCD's L2 copy of the
-  // slot's K/V.  With a launch order, each XCD's items run heaviest first; without
-  // one, pairs run one after another, each over its tiles.
+  // Workgroup i runs on XCD i % 8.  With at least 8 (KV head, slot) pairs, all row
+  // tiles of a pair go to the same XCD (pair p -> XCD p % 8) so they share that XCD's
+  // L2 copy of the slot's K/V.  With a launch order, items run heaviest first (per XCD
+  // when pairs keep their XCD); without one, pairs run one after another.
   int pair, tile_id;
   if (p.order) {
     const int code = p.order[blockIdx.x];
     if (code < 0) return;
     pair = code / n_tiles;
     tile_id = code - pair * n_tiles;
-  } else {
+  } else if (n_pairs >= kXcds) {
     const int xcd = blockIdx.x % kXcds;
     const int j = blockIdx.x / kXcds;
     pair = (j / n_tiles) * kXcds + xcd;
     tile_id = n_tiles - 1 - (j % n_tiles);
     if (pair >= n_pairs) return;
+  } else {
+    // fewer pairs than XCDs: items go round-robin over all XCDs (a pair's K/V is then
+    // cached by several L2s, which beats leaving XCDs idle)
+    pair = blockIdx.x / n_tiles;
+    tile_id = n_tiles - 1 - blockIdx.x % n_tiles;
   }
   const int g = pair % p.n_kv_heads;
   const int slot = pair / p.n_kv_heads;
@@ -360,7 +365,9 @@ int64_t fwd_bf16_grid(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
                       int32_t n_kv_heads, int32_t n_out) {
   const int64_t n_rows = int64_t(n_blocks) * block_size * (n_q_heads / n_kv_heads);
   const int64_t n_tiles = (n_rows + ROWS - 1) / ROWS;
-  const int64_t per_xcd = (int64_t(n_kv_heads) * n_out + kXcds - 1) / kXcds;
+  const int64_t n_pairs = int64_t(n_kv_heads) * n_out;
+  if (n_pairs < kXcds) return n_pairs * n_tiles;  // round-robin over XCDs
+  const int64_t per_xcd = (n_pairs + kXcds - 1) / kXcds;
   return kXcds * per_xcd * n_tiles;
 }
 

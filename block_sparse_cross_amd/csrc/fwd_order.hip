@@ -68,12 +68,17 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
   }
   __syncthreads();
 
-  // ---- workgroup slot bid holds, in the natural order, item (pair, tile) below
+  // ---- workgroup slot bid holds, in the natural order, item (pair, tile) below.  With
+  // fewer pairs than XCDs, slots are one list (items round-robin over XCDs, nx = 1);
+  // otherwise each XCD's slots are sorted separately (nx = kXcds).
+  const bool per_xcd_lists = n_pairs >= kXcds;
+  const int nx = per_xcd_lists ? kXcds : 1;
   const int per_xcd = (n_pairs + kXcds - 1) / kXcds;
-  const int n_bids = kXcds * per_xcd * n_tiles;
+  const int n_bids = per_xcd_lists ? kXcds * per_xcd * n_tiles : n_pairs * n_tiles;
   auto key_of = [&](int bid, int* code) {
-    const int xcd = bid % kXcds, j = bid / kXcds;
-    const int pair = (j / n_tiles) * kXcds + xcd;
+    const int xcd = per_xcd_lists ? bid % kXcds : 0;
+    const int j = per_xcd_lists ? bid / kXcds : bid;
+    const int pair = per_xcd_lists ? (j / n_tiles) * kXcds + xcd : j / n_tiles;
     const int tile = n_tiles - 1 - j % n_tiles;
     if (pair >= n_pairs) {
       *code = -1;
@@ -90,10 +95,10 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
   for (int bid = tid; bid < n_bids; bid += kThreads) {
     int code;
     const int key = key_of(bid, &code);
-    atomicAdd(&pos[bid % kXcds][key][wave], 1);
+    atomicAdd(&pos[bid % nx][key][wave], 1);
   }
   __syncthreads();
-  if (wave < kXcds) {
+  if (wave < nx) {
     const int x = wave, key = kKeys - 1 - lane;
     int own = 0;
 #pragma unroll
@@ -115,9 +120,9 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
   for (int bid = tid; bid < n_bids; bid += kThreads) {
     int code;
     const int key = key_of(bid, &code);
-    const int x = bid % kXcds;
+    const int x = bid % nx;
     const int at = atomicAdd(&pos[x][key][wave], 1);
-    order[at * kXcds + x] = code;
+    order[at * nx + x] = code;
   }
 }
 
@@ -130,7 +135,9 @@ hipError_t launch_fwd_order(const FwdParams& p, int32_t* order, hipStream_t stre
   const int64_t n_out = int64_t(p.n_slots) + p.has_self;
   if (n_tiles * n_out > kOrderMaxItems) return hipErrorInvalidValue;
   const int64_t n_pairs = int64_t(p.n_kv_heads) * n_out;
-  if (kXcds * ((n_pairs + kXcds - 1) / kXcds) * n_tiles > 0x7fffffff) return hipErrorInvalidValue;
+  if (fwd_bf16_grid(p.n_blocks, p.block_size, p.n_q_heads, p.n_kv_heads, int32_t(n_out)) >
+      0x7fffffff)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(fwd_order_kernel, dim3(1), dim3(kThreads), 0, stream, p, order,
                      int(n_tiles), int(n_pairs));
   return hipGetLastError();

@@ -18,7 +18,7 @@ import oracle
 from block_sparse_cross_amd.pipeline import make_plan
 from parity_helpers import (compare_partials, log, oracle_plan, sample_pairs, shape_of,
                             tolerances, upload)
-from workloads import CONFIGS, make_workload
+from workloads import CONFIGS, get_config, make_workload
 from workloads.gen import custom_workload, draw_merge_sets
 
 pytestmark = pytest.mark.gpu
@@ -212,6 +212,20 @@ def test_forward_launch_order_full():
     ro, rl = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
                                   wl.ctx_begin, 16, np.asarray(starts), np.asarray(lens),
                                   slot_of, n_slots, with_self=True)
+    tol_o, tol_l = tolerances("bf16")
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_o, tol_l, "partials")
+
+
+def test_forward_context_sweep_point_sampled():
+    """One point of the fixed-query-budget context sweep (512 draft queries over S = 2^18 keys,
+    LPT over 16 bins), on sampled (block, KV head) pairs."""
+    wl = make_workload(get_config("sweep_s262144"))
+    log(f"forward bf16, {wl.cfg.name} (sampled block/head pairs)")
+    ref = oracle_plan(wl)
+    dev, k_loc, v_loc, starts, lens, o, lse = _run_forward(wl, ref)
+    pairs = sample_pairs(wl, 4, seed=7)
+    ro, rl = _oracle_partials(wl, k_loc, v_loc, starts, lens, ref["slot_of"], ref["n_slots"],
+                              True, pairs)
     tol_o, tol_l = tolerances("bf16")
     compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_o, tol_l, "partials")
 

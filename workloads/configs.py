@@ -95,12 +95,28 @@ CONFIGS = [
 ]
 
 
+# Fixed query budget, growing context (the query-context asymmetry the Split-KV page's
+# Abstract describes: acceptance stays stable as the context grows at a fixed query
+# budget): the a3b head shape with 32 anchors (512 draft queries) over S keys, chunks of
+# 1024 balanced by LPT over 16 bins.
+SWEEP_CTX = [16384, 32768, 65536, 131072, 262144, 524288, 1048576]
+
+
+def sweep_config(ctx_len: int) -> WorkloadConfig:
+    return WorkloadConfig(
+        name=f"sweep_s{ctx_len}", seed=6, ctx_len=ctx_len, n_q_heads=32, n_kv_heads=4,
+        head_dim=128, dtype="bf16", sigma=0.5, block_size=16, chunk_len=1024,
+        n_anchors=32, anchor_lo=256, anchor_hi=ctx_len, slot_mode="lpt", n_bins=16)
+
+
 def get_config(name_or_index) -> WorkloadConfig:
     if isinstance(name_or_index, int):
         return CONFIGS[name_or_index]
     for c in CONFIGS:
         if c.name == name_or_index:
             return c
+    if isinstance(name_or_index, str) and name_or_index.startswith("sweep_s"):
+        return sweep_config(int(name_or_index[len("sweep_s"):]))
     raise KeyError(name_or_index)
 
 
