@@ -338,26 +338,55 @@ bsx_status bsx_cost(const bsx_shape* shape, const int64_t* anchor, const int64_t
   return device_status(bsx::launch_cost(p, s), "cost kernel");
 }
 
-// The bf16 launch order (int32 per workgroup) follows the descriptor in the
-// workspace when the problem has at most kOrderMaxItems (row tile, slot) items;
-// sized for a self slot, so it fits either way.
-size_t fwd_order_bytes(const bsx_shape* shape, int32_t n_slots) {
-  if (!shape || shape->dtype != BSX_BF16 || shape->n_kv_heads < 1 || shape->n_blocks < 1)
-    return 0;
-  const int64_t n_out = int64_t(n_slots) + 1;
+// Forward workspace: the chunk table (when it is not inline), then for bf16 launches
+// the launch order (int32 per workgroup) and, for launches that may split items, the
+// piece list, the split tables and the pieces' partials.  Laid out for a given
+// number of output slots; bsx_fwd_workspace covers both with and without a self slot.
+struct FwdWs {
+  size_t order_off = 0, piece_off = 0, split_off = 0, part_o_off = 0, part_lse_off = 0;
+  bool order = false, split = false;
+  size_t total = 0;
+};
+
+FwdWs fwd_ws_layout(const bsx_shape* shape, const bsx_chunks* chunks, int64_t n_out) {
+  FwdWs w;
+  w.total = align_up(fwd_layout(chunks->n_slots, chunks->n_chunks).total, 256);
+  if (!shape || shape->dtype != BSX_BF16 || shape->n_kv_heads < 1 || shape->n_blocks < 1 ||
+      n_out < 1)
+    return w;
   const int64_t n_rows = int64_t(shape->n_blocks) * shape->block_size *
                          (shape->n_q_heads / shape->n_kv_heads);
   const int64_t n_tiles = (n_rows + bsx::kFwdRows - 1) / bsx::kFwdRows;
-  if (n_tiles * n_out > bsx::kOrderMaxItems) return 0;
-  return sizeof(int32_t) * size_t(bsx::fwd_bf16_grid(shape->n_blocks, shape->block_size,
-                                                     shape->n_q_heads, shape->n_kv_heads,
-                                                     int32_t(n_out)));
+  if (n_tiles * n_out > bsx::kOrderMaxItems) return w;
+  const bsx::FwdSplitLayout sl = bsx::fwd_split_layout(
+      shape->n_blocks, shape->block_size, shape->n_q_heads, shape->n_kv_heads, int32_t(n_out));
+  const int64_t grid = sl.split_capable
+                           ? sl.grid
+                           : bsx::fwd_bf16_grid(shape->n_blocks, shape->block_size,
+                                                shape->n_q_heads, shape->n_kv_heads,
+                                                int32_t(n_out));
+  w.order = true;
+  w.order_off = w.total;
+  w.total += align_up(sizeof(int32_t) * size_t(grid), 256);
+  if (sl.split_capable) {
+    w.split = true;
+    w.piece_off = w.total;
+    w.total += align_up(sl.piece_bytes, 256);
+    w.split_off = w.total;
+    w.total += align_up(sl.split_bytes, 256);
+    w.part_o_off = w.total;
+    w.total += align_up(sl.part_o_bytes, 256);
+    w.part_lse_off = w.total;
+    w.total += align_up(sl.part_lse_bytes, 256);
+  }
+  return w;
 }
 
 size_t bsx_fwd_workspace(const bsx_shape* shape, const bsx_chunks* chunks) {
   if (!chunks || chunks->n_chunks < 0 || chunks->n_slots < 0) return 0;
-  const size_t table = align_up(fwd_layout(chunks->n_slots, chunks->n_chunks).total, 256);
-  return table + align_up(fwd_order_bytes(shape, chunks->n_slots), 256);
+  const size_t with_self = fwd_ws_layout(shape, chunks, int64_t(chunks->n_slots) + 1).total;
+  const size_t without = fwd_ws_layout(shape, chunks, chunks->n_slots).total;
+  return with_self > without ? with_self : without;
 }
 
 bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, const void* v,
@@ -411,18 +440,30 @@ bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, co
   p.scale = resolve_scale(shape);
   p.scale_log2 = p.scale * kLog2e;
   p.order = nullptr;
+  p.piece = nullptr;
+  p.split = nullptr;
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
   if (shape->dtype == BSX_BF16) {
     // The ordering pass costs a few microseconds of latency; it pays off when items
-    // can differ widely in length, i.e. when a slot holds many key tiles.
-    if (max_slot_tiles(chunks) > kOrderMinSlotTiles &&
-        fwd_order_bytes(shape, chunks->n_slots) > 0) {
-      int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
-                                                  align_up(l.total, 256));
+    // can differ widely in length, i.e. when a slot holds many key tiles.  Launches
+    // with few items may also split long items into pieces (merged afterwards).
+    const FwdWs w = fwd_ws_layout(shape, chunks, n_out);
+    char* base = static_cast<char*>(ws);
+    if (max_slot_tiles(chunks) > kOrderMinSlotTiles && w.order) {
+      int32_t* order = reinterpret_cast<int32_t*>(base + w.order_off);
+      if (w.split) {
+        p.piece = reinterpret_cast<int32_t*>(base + w.piece_off);
+        p.split = reinterpret_cast<int32_t*>(base + w.split_off);
+        p.part_o = reinterpret_cast<float*>(base + w.part_o_off);
+        p.part_lse = reinterpret_cast<float*>(base + w.part_lse_off);
+      }
       e = bsx::launch_fwd_order(p, order, s);
       if (e != hipSuccess) return device_status(e, "forward launch-order kernel");
       p.order = order;
     }
     e = bsx::launch_fwd_bf16(p, s);
+    if (e == hipSuccess && p.split) e = bsx::launch_fwd_piece_merge(p, s);
   } else {
     e = bsx::launch_fwd_f32(p, s);
   }

@@ -37,6 +37,12 @@ constexpr int kFwdKeyTile = 64;
 constexpr int kXcds = 8;
 // The launch-order pass handles at most this many (row tile, output slot) items.
 constexpr int kOrderMaxItems = 32768;
+// Launches with fewer (KV head, slot) pairs than XCDs and fewer items than this may
+// split long items into pieces (about kSplitTargetPieces in all) that the piece
+// merge combines.
+constexpr int kSplitMaxItems = 1024;
+constexpr int kSplitTargetPieces = 2048;
+constexpr int kSplitMinPieceTiles = 16;
 
 // Forward problem as handed to the kernels.  The table holds slot_ptr[n_slots + 1]
 // (int32) at byte 0 and the non-empty chunks grouped by slot, in chunk index order,
@@ -63,6 +69,14 @@ struct FwdParams {
   float scale_log2;   // scale * log2(e)
   uint32_t entries_off;
   const int32_t* order;  // bf16 launch order (workgroup -> item), or null: natural order
+  // split launches (order pass output, else null): piece index per workgroup, and
+  // split[0] = tiles per piece P, split[4 + code] = first partial slot of item `code`
+  // (-1: not split); pieces of split items write normalized partials to part_o
+  // [slot][kFwdRows][head_dim] and part_lse [slot][kFwdRows]
+  const int32_t* piece;
+  const int32_t* split;
+  float* part_o;
+  float* part_lse;
   ChunkTable table;
 };
 
@@ -121,9 +135,26 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 // Workgroups of the bf16 forward launch (the length of its launch-order array).
 int64_t fwd_bf16_grid(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
                       int32_t n_kv_heads, int32_t n_out);
-// Fills `order` (fwd_bf16_grid entries) with the forward's workgroup -> item map,
-// heaviest items first within each XCD; p.order is ignored.
+// Forward launch layout when items may be split (else split_capable is false):
+// the grid, and the workspace of the order pass's split tables and the partials.
+struct FwdSplitLayout {
+  bool split_capable;
+  int64_t grid;           // workgroups: items + kSplitTargetPieces
+  int64_t n_codes;        // item codes: pairs x row tiles
+  int64_t part_slots;     // partial slots of split items
+  size_t piece_bytes;     // int32 [grid]
+  size_t split_bytes;     // int32: header[4], sbase[n_codes], pcount[n_codes], list[n_codes]
+  size_t part_o_bytes;    // f32 [part_slots][kFwdRows][128]
+  size_t part_lse_bytes;  // f32 [part_slots][kFwdRows]
+};
+FwdSplitLayout fwd_split_layout(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t n_out);
+// Fills `order` (grid entries) with the forward's workgroup -> item map, heaviest
+// first (within each XCD when pairs keep their XCD); with p.piece/p.split non-null
+// (split launches) also the pieces and split tables.  p.order is ignored.
 hipError_t launch_fwd_order(const FwdParams& p, int32_t* order, hipStream_t stream);
+// Combines the pieces of each split item into o_part / lse_part (split launches).
+hipError_t launch_fwd_piece_merge(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
                             const float* o_parts, const float* lse_parts, float* o_out,

@@ -96,12 +96,13 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
   // tiles of a pair go to the same XCD (pair p -> XCD p % 8) so they share that XCD's
   // L2 copy of the slot's K/V.  With a launch order, items run heaviest first (per XCD
   // when pairs keep their XCD); without one, pairs run one after another.
-  int pair, tile_id;
+  int pair, tile_id, pj = 0;
   if (p.order) {
     const int code = p.order[blockIdx.x];
     if (code < 0) return;
     pair = code / n_tiles;
     tile_id = code - pair * n_tiles;
+    if (p.piece) pj = p.piece[blockIdx.x];
   } else if (n_pairs >= kXcds) {
     const int xcd = blockIdx.x % kXcds;
     const int j = blockIdx.x / kXcds;
@@ -184,12 +185,40 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
 
   const int64_t orow = (int64_t(slot) * n_q + qi) * p.n_q_heads + h;
 
+  // A split item's piece pj covers tiles [pj P, pj P + P) of the walk and writes a
+  // normalized partial of its own (slot sb + pj of part_o / part_lse).
+  const int sb = p.split ? p.split[4 + pair * n_tiles + tile_id] : -1;
+  const int P = p.split ? p.split[0] : 0;
+  const int64_t prow = (int64_t(sb + pj) * ROWS + wave * 32 + col);  // split: partial row
   TileWalk walk;
   walk.seg.init(p.table.dev ? p.table.dev : (const char*)(p.table.words),
                 p.entries_off, slot, is_self, mlo, mhi);
   bool have = mlo < mhi && walk.first();
+  int left = INT32_MAX;  // tiles this workgroup may still take
+  if (have && sb >= 0) {
+    int64_t skip = int64_t(pj) * P;
+    while (skip > 0) {
+      const int64_t in_seg = (walk.seg.seg1 - walk.p0 + KT - 1) / KT;
+      if (skip < in_seg) {
+        walk.p0 += skip * KT;
+        break;
+      }
+      skip -= in_seg;
+      if (!walk.seg.next()) {
+        have = false;
+        break;
+      }
+      walk.p0 = walk.seg.seg0;
+    }
+    left = P;
+  }
   if (!have) {
-    if (row_ok && half == 0) p.lse_part[orow] = -INFINITY;
+    if (row_ok && half == 0) {
+      if (sb >= 0)
+        p.part_lse[prow] = -INFINITY;
+      else
+        p.lse_part[orow] = -INFINITY;
+    }
     return;
   }
 
@@ -246,7 +275,7 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
   int stage = 0;
 
   while (have) {
-    const bool have_next = walk.advance();
+    const bool have_next = --left > 0 && walk.advance();
     Tile nxt = cur;
     if (have_next) {
       nxt = walk.tile();
@@ -344,10 +373,16 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (!row_ok) return;
   const bool has_keys = live && ltot > 0.f;
-  if (half == 0) p.lse_part[orow] = has_keys ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
+  const float lse_out = has_keys ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
+  if (half == 0) {
+    if (sb >= 0)
+      p.part_lse[prow] = lse_out;
+    else
+      p.lse_part[orow] = lse_out;
+  }
   if (!has_keys) return;
   const float inv = 1.f / ltot;
-  float* op = p.o_part + orow * D;
+  float* op = sb >= 0 ? p.part_o + prow * D : p.o_part + orow * D;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -377,8 +412,10 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const int64_t n_tiles = (n_rows + ROWS - 1) / ROWS;
   const int64_t n_out = int64_t(p.n_slots) + p.has_self;
   const int64_t n_pairs = int64_t(p.n_kv_heads) * n_out;
-  const int64_t grid = fwd_bf16_grid(p.n_blocks, p.block_size, p.n_q_heads, p.n_kv_heads,
-                                     int32_t(n_out));
+  const int64_t grid =
+      p.piece ? fwd_split_layout(p.n_blocks, p.block_size, p.n_q_heads, p.n_kv_heads,
+                                 int32_t(n_out)).grid
+              : fwd_bf16_grid(p.n_blocks, p.block_size, p.n_q_heads, p.n_kv_heads, int32_t(n_out));
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fwd_bf16_kernel, dim3(unsigned(grid)), dim3(THREADS), 0, stream, p,

@@ -15,6 +15,7 @@
 // meet only within a wave; suffix sums; scatter; equal counts keep no particular order).
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdint.h>
 
 #include "bsx_internal.h"
@@ -29,7 +30,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kTableLdsWords = 4096;  // chunk tables up to 16 KiB are read from LDS
 
 __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t* order,
-                                                             int n_tiles, int n_pairs) {
+                                                             int n_tiles, int n_pairs, int grid) {
   const BSX_KARG FwdParams& p = kernel_arg0<FwdParams>();
   __shared__ uint16_t work[kOrderMaxItems];
   __shared__ int32_t pos[kXcds][kKeys][kWaves];
@@ -68,6 +69,89 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
   }
   __syncthreads();
 
+  const int wave = tid >> 6, lane = tid & 63;
+  if (p.split) {
+    // ---- split launch (fewer pairs than XCDs, at most kThreads items): thread c owns
+    // item c = pair * n_tiles + tile.  P = max(min tiles, ceil(sum / target)); an item
+    // of w > P tiles becomes ceil(w / P) pieces, each of P tiles but the last.
+    __shared__ int64_t s_sum[kThreads];
+    __shared__ int s_scan[3][kThreads];
+    int32_t* piece = const_cast<int32_t*>(p.piece);
+    int32_t* split = const_cast<int32_t*>(p.split);
+    const int n_codes = n_pairs * n_tiles;
+    const int c = tid;
+    int w = 0;
+    if (c < n_codes) w = work[(c % n_tiles) * n_out + (c / n_tiles) / p.n_kv_heads];
+    s_sum[tid] = w;
+    __syncthreads();
+    for (int off = kThreads / 2; off > 0; off >>= 1) {
+      if (tid < off) s_sum[tid] += s_sum[tid + off];
+      __syncthreads();
+    }
+    int64_t P = (s_sum[0] + kSplitTargetPieces - 1) / kSplitTargetPieces;
+    P = P < kSplitMinPieceTiles ? kSplitMinPieceTiles : P;
+    const int pc = c < n_codes ? (w > P ? int((w + P - 1) / P) : 1) : 0;
+    const int own[3] = {pc, pc > 1 ? pc : 0, pc > 1 ? 1 : 0};
+    for (int k = 0; k < 3; ++k) s_scan[k][tid] = own[k];
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      int v[3];
+      for (int k = 0; k < 3; ++k) v[k] = tid >= off ? s_scan[k][tid - off] : 0;
+      __syncthreads();
+      for (int k = 0; k < 3; ++k) s_scan[k][tid] += v[k];
+      __syncthreads();
+    }
+    const int slot0 = s_scan[1][tid] - own[1], list_at = s_scan[2][tid] - own[2];
+    if (c < n_codes) {
+      split[4 + c] = pc > 1 ? slot0 : -1;
+      split[4 + n_codes + c] = pc;
+      if (pc > 1) split[4 + 2 * n_codes + list_at] = c;
+    }
+    const int total = s_scan[0][kThreads - 1];
+    if (tid == 0) {
+      split[0] = int32_t(P);
+      split[1] = total;
+      split[2] = s_scan[2][kThreads - 1];
+      split[3] = 0;
+    }
+    // counting sort of the pieces by their tile count, longest first (one list)
+    auto piece_key = [&](int j) {
+      const int64_t pw = pc > 1 ? (w - int64_t(j) * P < P ? w - int64_t(j) * P : P) : w;
+      return 1 + int(pw < kKeys - 2 ? pw : kKeys - 2);
+    };
+    for (int i = tid; i < kKeys * kWaves; i += kThreads) (&pos[0][0][0])[i] = 0;
+    __syncthreads();
+    for (int j = 0; j < pc; ++j) atomicAdd(&pos[0][piece_key(j)][wave], 1);
+    __syncthreads();
+    if (wave == 0) {
+      const int key = kKeys - 1 - lane;
+      int sum = 0;
+      for (int q = 0; q < kWaves; ++q) sum += pos[0][key][q];
+      int incl = sum;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      int acc = incl - sum;
+      for (int q = 0; q < kWaves; ++q) {
+        const int cnt = pos[0][key][q];
+        pos[0][key][q] = acc;
+        acc += cnt;
+      }
+    }
+    __syncthreads();
+    for (int j = 0; j < pc; ++j) {
+      const int at = atomicAdd(&pos[0][piece_key(j)][wave], 1);
+      order[at] = c;
+      piece[at] = j;
+    }
+    for (int i = total + tid; i < grid; i += kThreads) {
+      order[i] = -1;
+      piece[i] = 0;
+    }
+    return;
+  }
+
   // ---- workgroup slot bid holds, in the natural order, item (pair, tile) below.  With
   // fewer pairs than XCDs, slots are one list (items round-robin over XCDs, nx = 1);
   // otherwise each XCD's slots are sorted separately (nx = kXcds).
@@ -89,7 +173,6 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
     return 1 + (w < kKeys - 2 ? w : kKeys - 2);
   };
   static_assert(kKeys == 64, "one key per lane in the prefix pass");
-  const int wave = tid >> 6, lane = tid & 63;
   for (int i = tid; i < kXcds * kKeys * kWaves; i += kThreads) (&pos[0][0][0])[i] = 0;
   __syncthreads();
   for (int bid = tid; bid < n_bids; bid += kThreads) {
@@ -126,7 +209,85 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
   }
 }
 
+// ---- combine the pieces of each split item (exact LSE merge of normalized partials):
+// LSE = M + log sum_j exp(LSE_j - M), O = sum_j exp(LSE_j - LSE) O_j over pieces with
+// finite LSE.  One workgroup per (split item, 32 of its rows); a lane owns 16 columns.
+constexpr int kMergeRows = 32;
+
+__global__ __launch_bounds__(256) void fwd_piece_merge_kernel(FwdParams, int n_tiles, int n_codes) {
+  const BSX_KARG FwdParams& p = kernel_arg0<FwdParams>();
+  const int32_t* split = p.split;
+  const int m = blockIdx.x / (kFwdRows / kMergeRows);
+  const int rg = blockIdx.x % (kFwdRows / kMergeRows);
+  if (m >= split[2]) return;
+  const int code = split[4 + 2 * n_codes + m];
+  const int pc = split[4 + n_codes + code], sb = split[4 + code];
+  const int pair = code / n_tiles, tile = code % n_tiles;
+  const int G = p.n_q_heads / p.n_kv_heads;
+  const int g = pair % p.n_kv_heads, slot = pair / p.n_kv_heads;
+  const int64_t n_q = int64_t(p.n_blocks) * p.block_size;
+  const int row = rg * kMergeRows + (threadIdx.x >> 3), d0 = (threadIdx.x & 7) * 16;
+  const int64_t r = int64_t(tile) * kFwdRows + row;
+  if (r >= n_q * G) return;
+  float mx = -INFINITY;
+  for (int j = 0; j < pc; ++j) mx = fmaxf(mx, p.part_lse[int64_t(sb + j) * kFwdRows + row]);
+  const int64_t qi = r / G;
+  const int h = g * G + int(r % G);
+  const int64_t orow = (int64_t(slot) * n_q + qi) * p.n_q_heads + h;
+  if (mx == -INFINITY) {
+    if ((threadIdx.x & 7) == 0) p.lse_part[orow] = -INFINITY;
+    return;
+  }
+  float ssum = 0.f;
+  for (int j = 0; j < pc; ++j) {
+    const float l = p.part_lse[int64_t(sb + j) * kFwdRows + row];
+    if (l != -INFINITY) ssum += expf(l - mx);
+  }
+  const float lse = mx + logf(ssum);
+  float4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < pc; ++j) {
+    const float l = p.part_lse[int64_t(sb + j) * kFwdRows + row];
+    if (l == -INFINITY) continue;  // an empty piece's O is never read
+    const float wgt = expf(l - lse);
+    const float* src = p.part_o + (int64_t(sb + j) * kFwdRows + row) * 128 + d0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 x = *reinterpret_cast<const float4*>(src + 4 * i);
+      acc[i].x = fmaf(wgt, x.x, acc[i].x);
+      acc[i].y = fmaf(wgt, x.y, acc[i].y);
+      acc[i].z = fmaf(wgt, x.z, acc[i].z);
+      acc[i].w = fmaf(wgt, x.w, acc[i].w);
+    }
+  }
+  float* dst = p.o_part + orow * 128 + d0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(dst + 4 * i) = acc[i];
+  if ((threadIdx.x & 7) == 0) p.lse_part[orow] = lse;
+}
+
 }  // namespace
+
+FwdSplitLayout fwd_split_layout(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t n_out) {
+  FwdSplitLayout l{};
+  if (n_kv_heads < 1 || n_blocks < 1 || block_size < 1 || n_out < 1) return l;
+  const int64_t n_rows = int64_t(n_blocks) * block_size * (n_q_heads / n_kv_heads);
+  const int64_t n_tiles = (n_rows + kFwdRows - 1) / kFwdRows;
+  const int64_t n_pairs = int64_t(n_kv_heads) * n_out;
+  l.n_codes = n_pairs * n_tiles;
+  l.split_capable = n_pairs < kXcds && l.n_codes <= kSplitMaxItems;
+  if (!l.split_capable) return l;
+  l.grid = l.n_codes + kSplitTargetPieces;
+  // pieces of split items: each has w > P, so ceil(w / P) < 2 w / P, summing below 2 x target
+  l.part_slots = 2 * int64_t(kSplitTargetPieces);
+  l.piece_bytes = sizeof(int32_t) * size_t(l.grid);
+  l.split_bytes = sizeof(int32_t) * size_t(4 + 3 * l.n_codes);
+  l.part_o_bytes = sizeof(float) * size_t(l.part_slots) * kFwdRows * 128;
+  l.part_lse_bytes = sizeof(float) * size_t(l.part_slots) * kFwdRows;
+  return l;
+}
 
 hipError_t launch_fwd_order(const FwdParams& p, int32_t* order, hipStream_t stream) {
   const int G = p.n_q_heads / p.n_kv_heads;
@@ -135,11 +296,33 @@ hipError_t launch_fwd_order(const FwdParams& p, int32_t* order, hipStream_t stre
   const int64_t n_out = int64_t(p.n_slots) + p.has_self;
   if (n_tiles * n_out > kOrderMaxItems) return hipErrorInvalidValue;
   const int64_t n_pairs = int64_t(p.n_kv_heads) * n_out;
-  if (fwd_bf16_grid(p.n_blocks, p.block_size, p.n_q_heads, p.n_kv_heads, int32_t(n_out)) >
-      0x7fffffff)
-    return hipErrorInvalidValue;
+  int64_t grid = fwd_bf16_grid(p.n_blocks, p.block_size, p.n_q_heads, p.n_kv_heads,
+                               int32_t(n_out));
+  if (p.split) {
+    const FwdSplitLayout l = fwd_split_layout(p.n_blocks, p.block_size, p.n_q_heads,
+                                              p.n_kv_heads, int32_t(n_out));
+    if (!l.split_capable || !p.piece) return hipErrorInvalidValue;
+    grid = l.grid;
+  }
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fwd_order_kernel, dim3(1), dim3(kThreads), 0, stream, p, order,
-                     int(n_tiles), int(n_pairs));
+                     int(n_tiles), int(n_pairs), int(grid));
+  return hipGetLastError();
+}
+
+}  // namespace bsx
+
+namespace bsx {
+
+hipError_t launch_fwd_piece_merge(const FwdParams& p, hipStream_t stream) {
+  const int64_t n_out = int64_t(p.n_slots) + p.has_self;
+  const FwdSplitLayout l = fwd_split_layout(p.n_blocks, p.block_size, p.n_q_heads,
+                                            p.n_kv_heads, int32_t(n_out));
+  if (!l.split_capable || !p.split) return hipErrorInvalidValue;
+  const int G = p.n_q_heads / p.n_kv_heads;
+  const int64_t n_tiles = (int64_t(p.n_blocks) * p.block_size * G + kFwdRows - 1) / kFwdRows;
+  hipLaunchKernelGGL(fwd_piece_merge_kernel, dim3(unsigned(l.n_codes * (kFwdRows / kMergeRows))),
+                     dim3(256), 0, stream, p, int(n_tiles), int(l.n_codes));
   return hipGetLastError();
 }
 

@@ -230,6 +230,41 @@ def test_forward_context_sweep_point_sampled():
     compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_o, tol_l, "partials")
 
 
+@pytest.mark.parametrize("with_self", [False, True])
+def test_forward_split_pieces_full(with_self):
+    """A launch with fewer (KV head, slot) pairs than XCDs and long items: the launch-order
+    pass cuts items of more than P = 16 key tiles into pieces and the piece merge combines
+    them.  One slot of four 2048-key chunks (non-contiguous, rank-like), 16 anchors; compared
+    in full."""
+    S = 16384
+    rng = np.random.default_rng(31)
+    anchor = np.sort(rng.choice(S, 16, replace=False)).astype(np.int64)
+    anchor[0], anchor[-1] = 0, S
+    begin = np.zeros(16, np.int64)
+    begin[5] = 3000  # one block with a late context start
+    starts, lens = [2048, 6144, 10240, 14336], [2048] * 4
+    hk = 2 if with_self else 4
+    wl = custom_workload(seed=32, ctx_len=S, n_q_heads=32, n_kv_heads=hk, block_size=16,
+                         anchor=anchor.tolist(), ctx_begin=begin.tolist(), chunk_start=starts,
+                         chunk_len=lens)
+    k_loc, v_loc = wl.kv_chunks()
+    dev = upload(wl, k_loc, v_loc)
+    ch = bsx.Chunks(starts, lens, [0, 0, 0, 0], 1)
+    log(f"forward bf16, split pieces (self slot: {with_self})")
+    ks = dev["k_self"] if with_self else None
+    vs = dev["v_self"] if with_self else None
+    o, lse = bsx.attn_fwd(shape_of(wl), dev["q"], dev["k"], dev["v"], ks, vs, dev["anchor"],
+                          dev["ctx_begin"], ch)
+    o2, lse2 = bsx.attn_fwd(shape_of(wl), dev["q"], dev["k"], dev["v"], ks, vs, dev["anchor"],
+                            dev["ctx_begin"], ch)
+    assert torch.equal(lse, lse2)  # the order changes no value
+    ro, rl = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, 16, np.asarray(starts), np.asarray(lens),
+                                  np.zeros(4, np.int64), 1, with_self=with_self)
+    tol_o, tol_l = tolerances("bf16")
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_o, tol_l, "partials")
+
+
 # ----------------------------------------------------------------------------- edge cases
 
 EDGE_CASES = {
