@@ -491,8 +491,8 @@ size_t bsx_bwd_workspace(const bsx_shape* shape, const bsx_chunks* chunks) {
       shape->n_q_heads < 0)
     return 0;
   const size_t ent = align_up(sizeof(bsx::ChunkEntry) * size_t(chunks->n_chunks), 256);
-  const size_t delta =
-      align_up(sizeof(float) * size_t(shape->n_blocks) * shape->block_size * shape->n_q_heads, 256);
+  const size_t delta = align_up(
+      2 * sizeof(float) * size_t(shape->n_blocks) * shape->block_size * shape->n_q_heads, 256);
   const bsx::DqLayout l = bsx::bwd_dq_layout(shape->n_blocks, shape->block_size,
                                              shape->n_q_heads, shape->n_kv_heads);
   return ent + delta + align_up(l.plan_bytes, 256) + align_up(l.part_bytes, 256) + 256;
@@ -552,9 +552,9 @@ bsx_status bsx_attn_bwd(const bsx_shape* shape, const void* q, const void* k, co
   p.dv = dv;
   p.dk_self = dk_self;
   p.dv_self = dv_self;
-  p.delta = reinterpret_cast<float*>(static_cast<char*>(ws) + ent_bytes);
-  const size_t delta_bytes =
-      align_up(sizeof(float) * size_t(shape->n_blocks) * shape->block_size * shape->n_q_heads, 256);
+  p.stats = reinterpret_cast<float*>(static_cast<char*>(ws) + ent_bytes);
+  const size_t delta_bytes = align_up(
+      2 * sizeof(float) * size_t(shape->n_blocks) * shape->block_size * shape->n_q_heads, 256);
   const bsx::DqLayout dl = bsx::bwd_dq_layout(shape->n_blocks, shape->block_size,
                                               shape->n_q_heads, shape->n_kv_heads);
   p.dq_plan = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ent_bytes + delta_bytes);

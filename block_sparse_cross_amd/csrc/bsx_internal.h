@@ -96,7 +96,7 @@ struct BwdParams {
   float* dv;
   float* dk_self;
   float* dv_self;
-  float* delta;               // workspace [N_q][H_q]: rowsum(dO * O)
+  float* stats;               // workspace [N_q][H_q][2]: log2-domain LSE, rowsum(dO * O)
   int32_t* dq_plan;           // workspace: dQ work split (bwd_dq_layout)
   float* dq_part;             // workspace: partial dQ of split row tiles
   int64_t ctx_len;

@@ -10,14 +10,15 @@
 // subset (one rank's local keys) this gives exact local dK/dV and that share of dQ.
 //
 // Three kernels, no atomics (results are deterministic):
-//   delta: D_r = rowsum(dO * O).
-//   dkdv:  key-major.  A workgroup owns 128 local keys of one KV head (32 per wave,
-//          K/V rows kept in registers as MFMA operands) and walks the draft blocks
-//          whose range reaches its keys, 32 query rows at a time staged in LDS.
-//          S = Q K^T and dP = dO V^T put keys in lane columns, so the mask is one
-//          predicate per lane; dV^T += dO^T P and dK^T += Q^T dS read dO^T / Q^T
-//          with LDS transpose loads.  The draft blocks' own keys are extra tiles
-//          whose only rows are their block's.
+//   delta: D_r = rowsum(dO * O), stored with the row's log2-domain LSE.
+//   dkdv:  key-major.  A workgroup owns 64 local keys of one KV head, 32 per wave
+//          pair, and walks the draft blocks whose range reaches its keys, 32 query
+//          rows at a time streamed into LDS.  In a pair one wave computes P and dV,
+//          the other dP, dS and dK (P passes through LDS).  S = Q K^T and
+//          dP = dO V^T put keys in lane columns, so the mask is one predicate per
+//          lane; dV^T += dO^T P and dK^T += Q^T dS read dO^T / Q^T with LDS
+//          transpose loads.  The draft blocks' own keys are extra tiles whose only
+//          rows are their block's.
 //   dq:    query-major, shaped like the forward kernel: 128 rows per workgroup,
 //          K/V tiles of 64 keys in LDS; S^T = K Q^T and dP^T = V dO^T put rows in
 //          lane columns, dQ^T += K^T dS^T reads K^T with transpose loads.  A
@@ -41,10 +42,17 @@ constexpr int D = 128;
 constexpr int THREADS = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// ---------------------------------------------------------------- delta
+// log2-domain LSE of a row; rows with no visible key get +inf so that P = 0.
+__device__ inline float row_lse2(float lse) {
+  return lse == -INFINITY ? INFINITY : lse * kLog2e;
+}
+
+// ---------------------------------------------------------------- row statistics
+// stats[r] = (log2-domain LSE, D_r = rowsum(dO * O)) of query row r = q * H_q + h.
 __global__ __launch_bounds__(THREADS) void bwd_delta_kernel(const float* __restrict__ o,
                                                             const uint16_t* __restrict__ d_o,
-                                                            float* __restrict__ delta,
+                                                            const float* __restrict__ lse,
+                                                            float2* __restrict__ stats,
                                                             int64_t n_rows) {
   const int64_t row = int64_t(blockIdx.x) * (THREADS / 32) + (threadIdx.x >> 5);
   const int c = (threadIdx.x & 31) * 4;
@@ -58,33 +66,100 @@ __global__ __launch_bounds__(THREADS) void bwd_delta_kernel(const float* __restr
     acc = fmaf(ov.w, __uint_as_float(dv.y & 0xffff0000u), acc);
   }
   for (int off = 16; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if ((threadIdx.x & 31) == 0 && row < n_rows) delta[row] = acc;
-}
-
-// log2-domain LSE of a row; rows with no visible key get +inf so that P = 0.
-__device__ inline float row_lse2(float lse) {
-  return lse == -INFINITY ? INFINITY : lse * kLog2e;
+  if ((threadIdx.x & 31) == 0 && row < n_rows) stats[row] = make_float2(row_lse2(lse[row]), acc);
 }
 
 // ---------------------------------------------------------------- dK / dV
-constexpr int KV_KEYS = 128;   // keys per workgroup (32 per wave)
-constexpr int RS = 32;         // query rows per staged sub-tile
-constexpr int RP = 272;        // LDS pitch (bytes) of a staged Q / dO row
+// A workgroup owns KV_KEYS local keys of one KV head as two wave pairs of 32 keys.
+// The two waves of a pair split the work of the pair's keys by role:
+//   role A (even wave): S = Q K^T -> P (masked, bf16) -> dV^T += dO^T P,
+//   role B (odd wave):  dP = dO V^T, then with A's P: dS = P (dP - D) -> dK^T += Q^T dS,
+// so each wave holds one 32 x 128 f32 accumulator and one of K / V as operands (two
+// workgroups fit a CU).  P crosses from A to B through LDS once per step, as the
+// bf16 values the dV product uses (dS is formed from those same values).
+// The Q / dO rows of a step (32 query rows of one draft block) and their row
+// statistics stream into four LDS stages with direct-to-LDS loads issued two steps
+// ahead; one barrier per step publishes both A's P and the stage of the next step.
+// Key positions come from a binary search of the chunk table (from an LDS copy when
+// the table is small); the prologue's barriers wait for LDS traffic only, so the K / V
+// operand loads arrive while the window of draft blocks is compacted.
+constexpr int KV_KEYS = 64;   // keys per workgroup
+constexpr int RS = 32;        // query rows per step
+constexpr int ROW_B = D * 2;  // staged Q / dO row: 16 chunks of 16 bytes
+constexpr int WIN = 128;      // draft blocks compacted per window
+constexpr int XP_BYTES = 2048;  // one pair's P of one step: [u][lane] x 16 bytes
+constexpr int SEARCH_LDS = 256;  // chunk tables up to this size are searched in LDS
 
-__global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BwdParams, int n_ctx_tiles,
+// One stage.  Slot c of row r holds global chunk c ^ (r & 15), so the b128 row reads
+// and the transpose reads of the operands are free of bank conflicts.
+struct DkdvStage {
+  char q[RS * ROW_B];
+  char d_o[RS * ROW_B];
+  float lse2[RS];
+  float delta[RS];
+};
+
+// Joins the workgroup barrier once at most N vector-memory loads of this wave are in
+// flight and its LDS accesses are done.  Unlike __syncthreads it leaves the younger
+// direct-to-LDS prefetches outstanding.
+template <int N>
+__device__ inline void wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS traffic only: vector-memory loads in flight (the K / V
+// operands, prefetches) stay outstanding, unlike __syncthreads.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// The P exchange.  Written as LDS instructions the compiler does not track: it
+// would otherwise make every access to these buffers (which no direct-to-LDS load
+// targets) wait for all direct-to-LDS prefetches in flight.  The writes complete
+// before the next wait_barrier (lgkmcnt(0)); the reads wait for their own data.
+__device__ inline void xp_write(char* at, bf16x8 a, bf16x8 b) {
+  const uint32_t addr = uint32_t(reinterpret_cast<uintptr_t>(at));
+  asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024" ::"v"(addr),
+               "v"(__builtin_bit_cast(u32x4, a)), "v"(__builtin_bit_cast(u32x4, b))
+               : "memory");
+}
+__device__ inline void xp_read(const char* at, bf16x8* a, bf16x8* b) {
+  const uint32_t addr = uint32_t(reinterpret_cast<uintptr_t>(at));
+  u32x4 x, y;
+  asm volatile(
+      "ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(x), "=&v"(y)
+      : "v"(addr)
+      : "memory");
+  *a = __builtin_bit_cast(bf16x8, x);
+  *b = __builtin_bit_cast(bf16x8, y);
+}
+
+__global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_ctx_tiles,
                                                               int self_tiles_per_block) {
   const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
-  __shared__ __attribute__((aligned(16))) char sq[2][RS * RP];
-  __shared__ __attribute__((aligned(16))) char sdo[2][RS * RP];
-  __shared__ __attribute__((aligned(16))) float s_lse2[2][RS];
-  __shared__ __attribute__((aligned(16))) float s_delta[2][RS];
-  __shared__ int s_blocks[THREADS];
-  __shared__ int64_t s_blo[THREADS], s_bhi[THREADS];
+  // four stages as distinct arrays: loads into one provably never alias reads of another
+  __shared__ __attribute__((aligned(16))) DkdvStage stg0;
+  __shared__ __attribute__((aligned(16))) DkdvStage stg1;
+  __shared__ __attribute__((aligned(16))) DkdvStage stg2;
+  __shared__ __attribute__((aligned(16))) DkdvStage stg3;
+  __shared__ __attribute__((aligned(16))) char xp0[2 * XP_BYTES];  // P of even steps
+  __shared__ __attribute__((aligned(16))) char xp1[2 * XP_BYTES];  // P of odd steps
+  __shared__ int s_blocks[WIN];
+  __shared__ int64_t s_blo[WIN], s_bhi[WIN];
   __shared__ int s_wcount[4];
-  __shared__ int64_t s_red[4][2];
+  __shared__ int64_t s_red[2][2];
+  __shared__ uint32_t s_eoff[SEARCH_LDS];  // a small chunk table: local offsets ...
+  __shared__ int64_t s_estart[SEARCH_LDS];  // ... and context starts
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copies
+  const int pair = wave_u >> 1;
+  const bool role_b = (wave_u & 1) != 0;
   const int Hkv = p.n_kv_heads, Hq = p.n_q_heads, G = Hq / Hkv, B = p.block_size;
   const int g = blockIdx.x % Hkv;
   const int t = blockIdx.x / Hkv;
@@ -104,21 +179,91 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BwdParams, int n_c
     key0 = int64_t(self_block) * B + int64_t(st % self_tiles_per_block) * KV_KEYS;
     key_end = int64_t(self_block + 1) * B;
   }
-  const int kk = wave * 32 + col;
+  const int kk = pair * 32 + col;
   const int64_t krow = key0 + kk;
   const bool kvalid = krow < key_end;
-  int64_t kpos = krow;
-  if (!is_self && kvalid) {
-    int lo = 0, hi = p.n_entries - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (int64_t(ent[mid].local_off) <= krow) lo = mid; else hi = mid - 1;
+  const bool pair_live = __any(kvalid);  // same in both waves of a pair
+
+  // ---- the first window's block ranges start loading (raw values, used later), a
+  // small chunk table goes to LDS
+  const int scan_begin = is_self ? self_block : 0;
+  const int scan_end = is_self ? self_block + 1 : p.n_blocks;
+  int64_t raw_a = 0, raw_z = 0;  // a block's ctx_begin and anchor
+  bool in_win = false;
+  auto load_ranges = [&](int w0) {
+    const int b = w0 + tid;
+    in_win = tid < WIN && b < scan_end;
+    if (in_win && !is_self) {
+      raw_a = p.ctx_begin[b];
+      raw_z = p.anchor[b];
     }
-    kpos = ent[lo].start + (krow - int64_t(ent[lo].local_off));
+  };
+  // visible range of the lane's block of the window, [blo, bhi)
+  int64_t blo = 0, bhi = 0;
+  auto finish_ranges = [&](int w0) {
+    if (!in_win) return;
+    if (is_self) {
+      blo = int64_t(w0 + tid) * B;
+      bhi = blo + B;
+    } else {
+      int64_t a = raw_a, z = raw_z;
+      a = a < 0 ? 0 : (a > p.ctx_len ? p.ctx_len : a);
+      z = z < a ? a : (z > p.ctx_len ? p.ctx_len : z);
+      blo = a;
+      bhi = z;
+    }
+  };
+  load_ranges(scan_begin);
+  const int n_ent = p.n_entries;
+  const bool lds_table = !is_self && n_ent <= SEARCH_LDS;
+  if (lds_table) {
+    for (int e = tid; e < n_ent; e += THREADS) {
+      const ChunkEntry c = ent[e];
+      s_eoff[e] = c.local_off;
+      s_estart[e] = c.start;
+    }
+  }
+  lds_barrier();
+
+  // ---- context position of the key (role A applies the mask): the last chunk whose
+  // local offset is at most the key's row
+  int64_t kpos = krow;
+  if (!is_self && kvalid && !role_b) {
+    int lo = 0, hi = n_ent - 1;
+    if (lds_table) {
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (int64_t(s_eoff[mid]) <= krow) lo = mid; else hi = mid - 1;
+      }
+      kpos = s_estart[lo] + (krow - int64_t(s_eoff[lo]));
+    } else {
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (int64_t(ent[mid].local_off) <= krow) lo = mid; else hi = mid - 1;
+      }
+      kpos = ent[lo].start + (krow - int64_t(ent[lo].local_off));
+    }
   }
 
-  // ---- position range of the workgroup's keys
+  // ---- K (role A) or V (role B) rows of this lane's key: MFMA B operands, dims
+  // 16 i + 8 half .. + 8; rows past the tile's end read as zero; they
+  // arrive while the window is compacted
+  const int64_t kstride = int64_t(Hkv) * D;
+  const uint32_t row_bytes = uint32_t(kstride * 2);
+  const int64_t nrows_tile = key_end - key0 < KV_KEYS ? key_end - key0 : KV_KEYS;
+  const void* kv_src = is_self ? (role_b ? p.v_self : p.k_self) : (role_b ? p.v : p.k);
+  bf16x8 kf[8];
   {
+    const uint32_t bytes = nrows_tile > 0 ? uint32_t(nrows_tile) * row_bytes : 0u;
+    const __amdgpu_buffer_rsrc_t kr =
+        make_rsrc(static_cast<const uint16_t*>(kv_src) + key0 * kstride + int64_t(g) * D, bytes);
+    const uint32_t off = uint32_t(kk) * row_bytes + 16 * half;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kf[i] = as_bf16x8(buffer_load16(kr, off + 32 * i));
+  }
+
+  // ---- position range of the workgroup's keys (from the role-A waves)
+  if (!role_b) {
     int64_t a = kvalid ? kpos : INT64_MAX, b = kvalid ? kpos : INT64_MIN;
     for (int off = 16; off >= 1; off >>= 1) {
       const int64_t a2 = __shfl_xor(a, off), b2 = __shfl_xor(b, off);
@@ -126,109 +271,53 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BwdParams, int n_c
       b = b2 > b ? b2 : b;
     }
     if (lane == 0) {
-      s_red[wave][0] = a;
-      s_red[wave][1] = b;
+      s_red[pair][0] = a;
+      s_red[pair][1] = b;
     }
   }
-  __syncthreads();
-  int64_t pmin = INT64_MAX, pmax = INT64_MIN;
-  for (int w = 0; w < 4; ++w) {
-    pmin = s_red[w][0] < pmin ? s_red[w][0] : pmin;
-    pmax = s_red[w][1] > pmax ? s_red[w][1] : pmax;
-  }
+  lds_barrier();
+  int64_t pmin = s_red[0][0] < s_red[1][0] ? s_red[0][0] : s_red[1][0];
+  int64_t pmax = s_red[0][1] > s_red[1][1] ? s_red[0][1] : s_red[1][1];
   pmin = uniform64(pmin);
   pmax = uniform64(pmax);
 
-  // ---- K / V rows of this lane's key as MFMA B operands (dims 16t + 8*half .. +8)
-  const int64_t kstride = int64_t(Hkv) * D;
-  const uint32_t row_bytes = uint32_t(kstride * 2);
-  const int64_t nrows_tile = key_end - key0 < KV_KEYS ? key_end - key0 : KV_KEYS;
-  const uint16_t* kbase = static_cast<const uint16_t*>(is_self ? p.k_self : p.k);
-  const uint16_t* vbase = static_cast<const uint16_t*>(is_self ? p.v_self : p.v);
-  bf16x8 kf[8], vf[8];
-  {
-    const uint32_t bytes = nrows_tile > 0 ? uint32_t(nrows_tile) * row_bytes : 0u;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + key0 * kstride + int64_t(g) * D, bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + key0 * kstride + int64_t(g) * D, bytes);
-    const uint32_t off = uint32_t(kk) * row_bytes + 16 * half;
+  f32x16 acc[4];  // dV^T (role A) or unscaled dK^T (role B): rows d, columns keys
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      kf[i] = as_bf16x8(buffer_load16(kr, off + 32 * i));
-      vf[i] = as_bf16x8(buffer_load16(vr, off + 32 * i));
-    }
-  }
-
-  f32x16 dk[4], dv[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    dk[db] = zero16();
-    dv[db] = zero16();
-  }
+  for (int db = 0; db < 4; ++db) acc[db] = zero16();
   const float c2 = p.scale_log2;
-  const int64_t n_q = int64_t(p.n_blocks) * B;
-  const int q_rd = col * RP + half * 16;          // b128 row reads of Q / dO
-  const int tr_rd = tr_lane_offset(lane, RP);     // transpose reads of Q^T / dO^T
-  const int ld_row = tid >> 3, ld_ch = (tid & 7) * 2;  // staging: row, first of 2 chunks
-
-  // ---- walk the draft blocks whose visible range reaches these keys, as a sequence
-  // of (block, 32-row sub-tile) steps; the Q / dO / LSE / D rows of step j + 1 are
-  // loaded into registers while step j computes, then stored to the other LDS stage
-  const int nr = B * G;                         // query rows of one draft block
+  const int nr = B * G;  // query rows of one draft block
   const int nsub = (nr + RS - 1) / RS;
-  const int scan_begin = is_self ? self_block : 0;
-  const int scan_end = is_self ? self_block + 1 : p.n_blocks;
-  u32x4 st_q[2], st_do[2];
-  float st_l2 = INFINITY, st_dl = 0.f;
-  // loads step j of the current window into the staging registers
-  auto load_step = [&](int j) {
-    const int blk = s_blocks[j / nsub];
-    const int rr = (j % nsub) * RS + ld_row;
-    const bool ok = rr < nr;
-    const int64_t r = int64_t(blk) * nr + rr;
-    const int64_t q = ok ? r / G : 0;
-    const int h = g * G + int(ok ? r % G : 0);
-    const int64_t base = (q * Hq + h) * D;
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + base;
-    const uint16_t* drow = static_cast<const uint16_t*>(p.d_o) + base;
+  // operand reads of a stage: b128 row read of row col, chunk 2 i + half, at
+  // (k_rd ^ 32 i); transpose read of rows 16 u + 8 hi + 4 half + tj / 4, chunk
+  // 4 db + c0, at (tr_rd[hi] ^ 64 db) + 4096 u
+  const int k_rd = col * ROW_B + 16 * (half ^ (col & 15));
+  int tr_rd[2];
+  {
+    const int tj = lane & 15, tg = lane >> 4;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      st_q[c] = u32x4{0u, 0u, 0u, 0u};
-      st_do[c] = u32x4{0u, 0u, 0u, 0u};
-      if (ok) {
-        st_q[c] = *reinterpret_cast<const u32x4*>(qrow + (ld_ch + c) * 8);
-        st_do[c] = *reinterpret_cast<const u32x4*>(drow + (ld_ch + c) * 8);
-      }
+    for (int hi2 = 0; hi2 < 2; ++hi2) {
+      const int rr = 8 * hi2 + 4 * half + (tj >> 2);
+      const int c0 = 2 * (tg & 1) + ((tj & 3) >> 1);
+      tr_rd[hi2] = rr * ROW_B + 16 * (c0 ^ rr) + 8 * (tj & 1);
     }
-    if ((tid & 7) == 0) {
-      st_l2 = ok && q < n_q ? row_lse2(p.lse[q * Hq + h]) : INFINITY;
-      st_dl = ok && q < n_q ? p.delta[q * Hq + h] : 0.f;
-    }
-  };
-  auto store_step = [&](int stage) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      *reinterpret_cast<u32x4*>(sq[stage] + ld_row * RP + (ld_ch + c) * 16) = st_q[c];
-      *reinterpret_cast<u32x4*>(sdo[stage] + ld_row * RP + (ld_ch + c) * 16) = st_do[c];
-    }
-    if ((tid & 7) == 0) {
-      s_lse2[stage][ld_row] = st_l2;
-      s_delta[stage][ld_row] = st_dl;
-    }
-  };
+  }
+  // staging: wave w fills rows 8 w .. 8 w + 7 of Q and of dO, four rows per load
+  // (lane: row 8 w + 4 i + lane / 16, slot lane % 16 <- chunk slot ^ (row & 15));
+  // wave 0 also loads the 32 rows' statistics (lane: row lane % 32, field lane / 32)
+  const uint32_t ld_chunk = uint32_t(((lane & 15) ^ (8 * (wave & 1)) ^ (lane >> 4)) * 16);
+  const int blk_elems = B * Hq * D;
+  const uint32_t blk_bytes = uint32_t(blk_elems) * 2u;
+  const uint32_t blk_stat_bytes = uint32_t(B * Hq) * 8u;
 
-  for (int wb = scan_begin; wb < scan_end && pmin <= pmax; wb += THREADS) {
+  for (int wb = scan_begin; wb < scan_end && pmin <= pmax; wb += WIN) {
     // ordered compaction of the hit blocks of this window (and their ranges)
-    const int b = wb + tid;
-    bool hit = false;
-    int64_t blo = 0, bhi = 0;
-    if (b < scan_end) {
-      visible_range(p.anchor, p.ctx_begin, p.ctx_len, B, is_self, b, &blo, &bhi);
-      hit = is_self || (blo < bhi && blo <= pmax && bhi > pmin);
-    }
+    if (wb != scan_begin) load_ranges(wb);
+    finish_ranges(wb);
+    const bool hit = in_win && (is_self || (blo < bhi && blo <= pmax && bhi > pmin));
     const uint64_t ball = __ballot(hit);
-    __syncthreads();  // the previous window is done with s_blocks and the stages
+    lds_barrier();  // the previous window is done with s_blocks, the stages and P
     if (lane == 0) s_wcount[wave] = __popcll(ball);
-    __syncthreads();
+    lds_barrier();
     int before = 0, total = 0;
     for (int w = 0; w < 4; ++w) {
       before += w < wave ? s_wcount[w] : 0;
@@ -236,80 +325,183 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BwdParams, int n_c
     }
     if (hit) {
       const int at = before + __popcll(ball & ((uint64_t(1) << lane) - 1));
-      s_blocks[at] = b;
+      s_blocks[at] = wb + tid;
       s_blo[at] = blo;
       s_bhi[at] = bhi;
     }
-    __syncthreads();
-
+    lds_barrier();
     const int nseq = total * nsub;
-    if (nseq > 0) {
-      load_step(0);
-      store_step(0);
-    }
-    __syncthreads();
-    for (int j = 0; j < nseq; ++j) {
-      const int stage = j & 1;
-      if (j + 1 < nseq) load_step(j + 1);
-      const int bi = j / nsub;
-      const bool key_vis = kvalid && kpos >= s_blo[bi] && kpos < s_bhi[bi];
-      if (__any(key_vis)) {
-        const char* q_s = sq[stage];
-        const char* do_s = sdo[stage];
-        f32x16 sacc = zero16(), dpacc = zero16();
+    if (nseq == 0) continue;
+
+    // loads of the next step in issue order into `dst`
+    int ib = 0, isub = 0;
+    auto issue = [&](DkdvStage& dst) {
+      const int blk = __builtin_amdgcn_readfirstlane(s_blocks[ib]);
+      const int64_t q0 = int64_t(blk) * B;  // the block's first query
+      const __amdgpu_buffer_rsrc_t qr =
+          make_rsrc(static_cast<const uint16_t*>(p.q) + q0 * Hq * D, blk_bytes);
+      const __amdgpu_buffer_rsrc_t dr =
+          make_rsrc(static_cast<const uint16_t*>(p.d_o) + q0 * Hq * D, blk_bytes);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          sacc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(q_s + q_rd + 32 * k)),
-                           kf[k], sacc);
-          dpacc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(do_s + q_rd + 32 * k)),
-                            vf[k], dpacc);
-        }
-        f32x16 pm, ds;
+      for (int i = 0; i < 2; ++i) {
+        const int rr = isub * RS + 8 * wave + 4 * i + (lane >> 4);  // row within the block
+        const int qq = rr / G;
+        const uint32_t off = rr < nr ? uint32_t(((qq * Hq + g * G + (rr - qq * G)) * D) * 2) +
+                                           (ld_chunk ^ uint32_t(64 * i))
+                                     : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            qr, (lds_void*)(dst.q + (8 * wave_u + 4 * i) * ROW_B), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            dr, (lds_void*)(dst.d_o + (8 * wave_u + 4 * i) * ROW_B), 16, off, 0, 0, 0);
+      }
+      if (wave_u == 0) {
+        const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.stats + q0 * Hq * 2, blk_stat_bytes);
+        const int rr = isub * RS + col;
+        const int qq = rr / G;
+        const uint32_t off =
+            rr < nr ? uint32_t(((qq * Hq + g * G + (rr - qq * G)) * 2 + half) * 4) : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void*)(dst.lse2), 4, off, 0, 0, 0);
+      }
+      if (++isub == nsub) {
+        isub = 0;
+        ++ib;
+      }
+    };
+
+    int j = 0, cb = 0, csub = 0;  // step computed next, its block index and sub-tile
+    // One step computes on stage `cur` and loads step j + 3 into `nx`; the barrier in
+    // its middle publishes A's P (buffer `xpb`) and the stage of step j + 1.
+    auto step = [&](DkdvStage& cur, DkdvStage& nx, char* xpb) -> bool {
+      char* xpp = xpb + pair * XP_BYTES;
+      f32x16 s = zero16();
+      bf16x8 pb[2];
+      bf16x4 tr[2][4][2];  // phase-2 transpose operands, read before the barrier
+      float4 st4[4];       // A: log2 LSE (+inf for an invisible key); B: D
+      if (pair_live && !role_b) {
+        u32x4 opd[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          opd[i] = *reinterpret_cast<const u32x4*>(cur.q + (k_rd ^ (32 * i)));
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          st4[a] = *reinterpret_cast<const float4*>(cur.lse2 + 8 * a + 4 * half);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = mfma_bf16(as_bf16x8(opd[i]), kf[i], s);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            tr[u][db][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(cur.d_o + ((tr_rd[0] ^ (64 * db)) + 4096 * u)));
+            tr[u][db][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(cur.d_o + ((tr_rd[1] ^ (64 * db)) + 4096 * u)));
+          }
+        // an invisible key gets P = exp2(x - inf) = 0
+        const int64_t vlo = s_blo[cb], vhi = s_bhi[cb];
+        const float koff = (kvalid & (kpos >= vlo) & (kpos < vhi)) ? 0.f : INFINITY;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const float4 l4 = *reinterpret_cast<const float4*>(s_lse2[stage] + 8 * a + 4 * half);
-          const float4 d4 = *reinterpret_cast<const float4*>(s_delta[stage] + 8 * a + 4 * half);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+          const float lv[4] = {st4[a].x + koff, st4[a].y + koff, st4[a].z + koff, st4[a].w + koff};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * a + e;
-            const float pv =
-                key_vis ? __builtin_amdgcn_exp2f(fmaf(sacc[v], c2, -lv[e])) : 0.f;
-            pm[v] = pv;
-            ds[v] = pv * (dpacc[v] - dd[e]);
+            s[v] = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -lv[e]));
           }
         }
+        pb[0] = pack_bf16(s, 0);
+        pb[1] = pack_bf16(s, 1);
+        xp_write(xpp + lane * 16, pb[0], pb[1]);
+      }
+      if (pair_live && role_b) {
+        u32x4 opd[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 pb = pack_bf16(pm, u);
-          const bf16x8 sb = pack_bf16(ds, u);
+        for (int i = 0; i < 8; ++i)
+          opd[i] = *reinterpret_cast<const u32x4*>(cur.d_o + (k_rd ^ (32 * i)));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = mfma_bf16(as_bf16x8(opd[i]), kf[i], s);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
-            dv[db] = mfma_bf16(tr_operand(do_s + tr_rd, RP, u, db * 64), pb, dv[db]);
-            dk[db] = mfma_bf16(tr_operand(q_s + tr_rd, RP, u, db * 64), sb, dk[db]);
+            tr[u][db][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(cur.q + ((tr_rd[0] ^ (64 * db)) + 4096 * u)));
+            tr[u][db][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(cur.q + ((tr_rd[1] ^ (64 * db)) + 4096 * u)));
+          }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          st4[a] = *reinterpret_cast<const float4*>(cur.delta + 8 * a + 4 * half);
+      }
+      if (j + 2 < nseq) {
+        if (wave_u == 0) wait_barrier<5>(); else wait_barrier<4>();
+      } else {
+        wait_barrier<0>();
+      }
+      if (j + 3 < nseq) issue(nx);
+      if (pair_live && role_b) {
+        xp_read(xpp + lane * 16, &pb[0], &pb[1]);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float dd[4] = {st4[a].x, st4[a].y, st4[a].z, st4[a].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * a + e;
+            s[v] = static_cast<float>(pb[v >> 3][v & 7]) * (s[v] - dd[e]);  // dS
           }
         }
+        pb[0] = pack_bf16(s, 0);
+        pb[1] = pack_bf16(s, 1);
       }
-      if (j + 1 < nseq) store_step(stage ^ 1);
-      __syncthreads();
+      if (pair_live) {
+        // A: dV^T += dO^T P;  B: dK^T += Q^T dS
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const bf16x4 lo4 = tr[u][db][0], hi4 = tr[u][db][1];
+            const bf16x8 a = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            acc[db] = mfma_bf16(a, pb[u], acc[db]);
+          }
+      }
+      if (++csub == nsub) {
+        csub = 0;
+        ++cb;
+      }
+      return ++j < nseq;
+    };
+
+    // prologue: steps 0 .. 2 in flight, step 0 published
+    issue(stg0);
+    if (nseq > 1) issue(stg1);
+    if (nseq > 2) issue(stg2);
+    if (nseq > 2) {
+      if (wave_u == 0) wait_barrier<10>(); else wait_barrier<8>();
+    } else if (nseq > 1) {
+      if (wave_u == 0) wait_barrier<5>(); else wait_barrier<4>();
+    } else {
+      wait_barrier<0>();
+    }
+    while (step(stg0, stg3, xp0) && step(stg1, stg0, xp1) && step(stg2, stg1, xp0) &&
+           step(stg3, stg2, xp1)) {
     }
   }
 
   if (!kvalid) return;
-  float* dkrow = (is_self ? p.dk_self : p.dk) + (krow * Hkv + g) * D;
-  float* dvrow = (is_self ? p.dv_self : p.dv) + (krow * Hkv + g) * D;
-  const float sc = p.scale;
+  float* dst = role_b ? (is_self ? p.dk_self : p.dk) : (is_self ? p.dv_self : p.dv);
+  dst += (krow * Hkv + g) * D;
+  const float sc = role_b ? p.scale : 1.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int d0 = db * 32 + 8 * a + 4 * half;
-      *reinterpret_cast<float4*>(dkrow + d0) =
-          make_float4(dk[db][4 * a] * sc, dk[db][4 * a + 1] * sc, dk[db][4 * a + 2] * sc,
-                      dk[db][4 * a + 3] * sc);
-      *reinterpret_cast<float4*>(dvrow + d0) =
-          make_float4(dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2], dv[db][4 * a + 3]);
+      *reinterpret_cast<float4*>(dst + d0) =
+          make_float4(acc[db][4 * a] * sc, acc[db][4 * a + 1] * sc, acc[db][4 * a + 2] * sc,
+                      acc[db][4 * a + 3] * sc);
     }
 }
 
@@ -356,8 +548,9 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
   const int64_t qi = row_ok ? r / G : 0;
   const int h = g * G + int(row_ok ? r % G : 0);
   const int64_t blk = qi / B;
-  const float lse2 = row_ok ? row_lse2(p.lse[qi * Hq + h]) : INFINITY;
-  const float dlt = row_ok ? p.delta[qi * Hq + h] : 0.f;
+  const float2 stat = row_ok ? reinterpret_cast<const float2*>(p.stats)[qi * Hq + h]
+                             : make_float2(INFINITY, 0.f);
+  const float lse2 = stat.x, dlt = stat.y;
 
   // Q^T and dO^T fragments of this lane's row (dims 16t + 8*half .. +8)
   bf16x8 qf[8], dof[8];
@@ -385,7 +578,6 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
   // Direct-to-LDS staging: wave w fills rows 16w .. 16w + 15 of a tile, four rows per
   // instruction, one 16-byte chunk per lane; slot c of LDS row r holds global chunk
   // c ^ (r & 15), so the b128 and transpose operand reads below are conflict-free.
-  typedef __attribute__((address_space(3))) void lds_void;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ld_row_off = uint32_t(16 * wave + (lane >> 4)) * row_bytes;
   const uint32_t ld_chunk = uint32_t(((lane & 15) ^ (lane >> 4)) * 16);
@@ -780,7 +972,8 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   if (n_rows > 0) {
     const int64_t blocks = (n_rows + (THREADS / 32) - 1) / (THREADS / 32);
     hipLaunchKernelGGL(bwd_delta_kernel, dim3(unsigned(blocks)), dim3(THREADS), 0, stream, p.o,
-                       static_cast<const uint16_t*>(p.d_o), p.delta, n_rows);
+                       static_cast<const uint16_t*>(p.d_o), p.lse,
+                       reinterpret_cast<float2*>(p.stats), n_rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
