@@ -177,24 +177,6 @@ float resolve_scale(const bsx_shape* s) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// bf16 forward launches whose largest slot spans more than this many 64-key tiles
-// run the launch-order pass first.  Measured: slots of 8 chunks x 1024 keys (items of
-// 0 to 128 tiles) gain 10%; one-chunk slots (items of at most 16 tiles, nearly all
-// full) lose 3% to the extra launch.
-constexpr int64_t kOrderMinSlotTiles = 32;
-
-int64_t max_slot_tiles(const bsx_chunks* c) {
-  std::vector<int64_t> tiles(size_t(c->n_slots), 0);
-  for (int32_t i = 0; i < c->n_chunks; ++i) {
-    if (c->len[i] <= 0) continue;
-    tiles[size_t(c->slot ? c->slot[i] : i)] +=
-        (c->len[i] + bsx::kFwdKeyTile - 1) / bsx::kFwdKeyTile;
-  }
-  int64_t m = 0;
-  for (int64_t t : tiles) m = t > m ? t : m;
-  return m;
-}
-
 }  // namespace
 
 extern "C" {
@@ -445,12 +427,13 @@ bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, co
   p.part_o = nullptr;
   p.part_lse = nullptr;
   if (shape->dtype == BSX_BF16) {
-    // The ordering pass costs a few microseconds of latency; it pays off when items
-    // can differ widely in length, i.e. when a slot holds many key tiles.  Launches
-    // with few items may also split long items into pieces (merged afterwards).
+    // The launch-order pass (heaviest items first on each XCD, empty items dropped)
+    // costs one small launch and pays for itself even when items are at most one chunk
+    // long (measured on 16 one-chunk LPT bins).  Launches with few items may also split
+    // long items into pieces (merged afterwards).
     const FwdWs w = fwd_ws_layout(shape, chunks, n_out);
     char* base = static_cast<char*>(ws);
-    if (max_slot_tiles(chunks) > kOrderMinSlotTiles && w.order) {
+    if (w.order) {
       int32_t* order = reinterpret_cast<int32_t*>(base + w.order_off);
       if (w.split) {
         p.piece = reinterpret_cast<int32_t*>(base + w.piece_off);

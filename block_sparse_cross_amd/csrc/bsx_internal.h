@@ -35,6 +35,13 @@ struct ChunkTable {
 constexpr int kFwdRows = 128;
 constexpr int kFwdKeyTile = 64;
 constexpr int kXcds = 8;
+// (KV head, slot) pair that XCD x runs in round `round` of the natural launch order:
+// rounds alternate direction over the XCDs, so a run of pairs whose work falls (or
+// rises) with the pair index, such as LPT bins filled heaviest first, is spread
+// evenly over the XCDs instead of piling its heavier half onto half of them.
+__host__ __device__ inline int pair_of_xcd_round(int round, int xcd) {
+  return round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
+}
 // The launch-order pass handles at most this many (row tile, output slot) items.
 constexpr int kOrderMaxItems = 32768;
 // Launches with fewer (KV head, slot) pairs than XCDs and fewer items than this may

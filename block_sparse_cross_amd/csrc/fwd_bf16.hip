@@ -93,20 +93,23 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
   const int half = lane >> 5, col = lane & 31;
 
   // Workgroup i runs on XCD i % 8.  With at least 8 (KV head, slot) pairs, all row
-  // tiles of a pair go to the same XCD (pair p -> XCD p % 8) so they share that XCD's
-  // L2 copy of the slot's K/V.  With a launch order, items run heaviest first (per XCD
+  // tiles of a pair go to the same XCD (pairs are dealt to the XCDs in rounds of 8,
+  // alternating direction) so they share that XCD's L2 copy of the slot's K/V.  With a launch order, items run heaviest first (per XCD
   // when pairs keep their XCD); without one, pairs run one after another.
   int pair, tile_id, pj = 0;
+  bool empty_item = false;
   if (p.order) {
-    const int code = p.order[blockIdx.x];
-    if (code < 0) return;
+    int code = p.order[blockIdx.x];
+    if (code == -1) return;
+    empty_item = code < -1;  // marked by the order pass: the item visits no key tile
+    if (empty_item) code = -2 - code;
     pair = code / n_tiles;
     tile_id = code - pair * n_tiles;
     if (p.piece) pj = p.piece[blockIdx.x];
   } else if (n_pairs >= kXcds) {
     const int xcd = blockIdx.x % kXcds;
     const int j = blockIdx.x / kXcds;
-    pair = (j / n_tiles) * kXcds + xcd;
+    pair = pair_of_xcd_round(j / n_tiles, xcd);
     tile_id = n_tiles - 1 - (j % n_tiles);
     if (pair >= n_pairs) return;
   } else {
@@ -127,6 +130,10 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
   const bool row_ok = r < n_rows;
   const int64_t qi = row_ok ? r / G : 0;
   const int h = g * G + int(row_ok ? r % G : 0);
+  if (empty_item) {  // (a split launch marks no item)
+    if (row_ok && half == 0) p.lse_part[(int64_t(slot) * n_q + qi) * p.n_q_heads + h] = -INFINITY;
+    return;
+  }
   int64_t lo = 0, hi = 0;
   if (row_ok)
     visible_range(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, is_self, qi / p.block_size,

@@ -8,7 +8,9 @@
 // of the chip.  This pass counts each item's tiles and sorts the workgroups of
 // each XCD by that count, largest first (longest-processing-time order), keeping
 // every item on the XCD the natural order gives it (its slot's K/V stays in that
-// XCD's L2).  The order changes no result, only the schedule.
+// XCD's L2).  Items that visit no tile come last and are marked, so their
+// workgroups skip straight to writing an empty partial.  The order changes no result,
+// only the schedule.
 //
 // One workgroup of 1024 threads: per-(row tile, slot) tile counts go to LDS, then a
 // counting sort on the clamped count per XCD (one LDS histogram per wave, so atomics
@@ -162,14 +164,16 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
   auto key_of = [&](int bid, int* code) {
     const int xcd = per_xcd_lists ? bid % kXcds : 0;
     const int j = per_xcd_lists ? bid / kXcds : bid;
-    const int pair = per_xcd_lists ? (j / n_tiles) * kXcds + xcd : j / n_tiles;
+    const int pair = per_xcd_lists ? pair_of_xcd_round(j / n_tiles, xcd) : j / n_tiles;
     const int tile = n_tiles - 1 - j % n_tiles;
     if (pair >= n_pairs) {
       *code = -1;
       return 0;
     }
-    *code = pair * n_tiles + tile;
     const int w = work[tile * n_out + pair / p.n_kv_heads];
+    // an item that visits no tile is marked (-2 - item): its workgroup only writes the
+    // rows' empty-partial LSE
+    *code = w > 0 ? pair * n_tiles + tile : -2 - (pair * n_tiles + tile);
     return 1 + (w < kKeys - 2 ? w : kKeys - 2);
   };
   static_assert(kKeys == 64, "one key per lane in the prefix pass");
