@@ -30,6 +30,7 @@ constexpr int kThreads = 1024;
 constexpr int kKeys = 64;   // sort key: 0 = no item, else 1 + min(tiles, 62)
 constexpr int kWaves = kThreads / 64;
 constexpr int kTableLdsWords = 4096;  // chunk tables up to 16 KiB are read from LDS
+constexpr int kRangeLdsBlocks = 1024;  // block ranges of launches up to this size, too
 
 __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t* order,
                                                              int n_tiles, int n_pairs, int grid) {
@@ -41,16 +42,24 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
   const int G = p.n_q_heads / p.n_kv_heads;
   const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
   __shared__ __attribute__((aligned(16))) uint32_t s_table[kTableLdsWords];
-  // the chunk table, copied to LDS when it fits: every lane walks it below
+  __shared__ int64_t s_blo[kRangeLdsBlocks], s_bhi[kRangeLdsBlocks];
+  // the chunk table and every block's visible range, copied to LDS when they fit (one
+  // round trip; every lane walks them below)
   const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
   const int64_t table_bytes =
       p.entries_off + int64_t(reinterpret_cast<const int32_t*>(table)[p.n_slots]) * 16;
-  if (table_bytes <= int64_t(sizeof(s_table))) {
+  const bool lds_table = table_bytes <= int64_t(sizeof(s_table));
+  const bool lds_ranges = p.n_blocks <= kRangeLdsBlocks;
+  if (lds_table) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(table);
     for (int i = tid; i < int(table_bytes / 4); i += kThreads) s_table[i] = src[i];
-    __syncthreads();
-    table = reinterpret_cast<const char*>(s_table);
   }
+  if (lds_ranges) {
+    for (int b = tid; b < p.n_blocks; b += kThreads)
+      visible_range(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, false, b, &s_blo[b], &s_bhi[b]);
+  }
+  if (lds_table || lds_ranges) __syncthreads();
+  if (lds_table) table = reinterpret_cast<const char*>(s_table);
   const int32_t* slot_ptr = reinterpret_cast<const int32_t*>(table);
   const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table + p.entries_off);
 
@@ -61,8 +70,20 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
     const bool is_self = p.has_self && slot == p.n_slots;
     const int64_t r0 = int64_t(tile) * kFwdRows;
     const int64_t r1 = r0 + kFwdRows < n_rows ? r0 + kFwdRows : n_rows;
-    int64_t mlo, mhi;
-    row_span_union(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, G, is_self, r0, r1, &mlo, &mhi);
+    int64_t mlo = INT64_MAX, mhi = INT64_MIN;
+    if (lds_ranges && !is_self) {
+      // the union of the ranges of the blocks of rows [r0, r1), from LDS
+      const int64_t b0 = r0 / G / p.block_size, b1 = (r1 - 1) / G / p.block_size;
+      for (int64_t b = b0; b <= b1; ++b) {
+        if (s_blo[b] < s_bhi[b]) {
+          mlo = s_blo[b] < mlo ? s_blo[b] : mlo;
+          mhi = s_bhi[b] > mhi ? s_bhi[b] : mhi;
+        }
+      }
+    } else {
+      row_span_union(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, G, is_self, r0, r1, &mlo,
+                     &mhi);
+    }
     int64_t tiles = 0;
     if (mlo < mhi)
       tiles = is_self ? (mhi - mlo + kFwdKeyTile - 1) / kFwdKeyTile
