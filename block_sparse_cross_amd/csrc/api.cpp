@@ -141,7 +141,11 @@ hipError_t place_table(const std::vector<uint32_t>& words, void* ws, hipStream_t
   return bsx::launch_upload(words.data(), words.size(), static_cast<uint32_t*>(ws), stream);
 }
 
-void build_fwd_descriptor(const bsx_chunks* c, std::vector<uint32_t>* words, int32_t* n_entries) {
+// Each slot's entries are sorted by start (ties keep chunk index order); *order is 2
+// when every slot's entries are also disjoint, else 1.  Kernels walking a slot stop at
+// its first entry past their range, and bisect to their first entry when disjoint.
+void build_fwd_descriptor(const bsx_chunks* c, std::vector<uint32_t>* words, int32_t* n_entries,
+                          int32_t* order) {
   const int32_t nc = c->n_chunks, ns = c->n_slots;
   const FwdLayout l = fwd_layout(ns, nc);
   std::vector<int64_t> off(nc);
@@ -162,6 +166,16 @@ void build_fwd_descriptor(const bsx_chunks* c, std::vector<uint32_t>* words, int
     const int32_t s = c->slot ? c->slot[i] : i;
     ent[fill[s]++] = bsx::ChunkEntry{c->start[i], uint32_t(c->len[i]), uint32_t(off[i])};
   }
+  bool disjoint = true;
+  for (int32_t s = 0; s < ns; ++s) {
+    const auto b = ent.begin() + ptr[s], z = ent.begin() + ptr[s + 1];
+    std::stable_sort(b, z, [](const bsx::ChunkEntry& x, const bsx::ChunkEntry& y) {
+      return x.start < y.start;
+    });
+    for (auto it = b; it + 1 < z; ++it)
+      if (it->start + int64_t(it->len) > (it + 1)->start) disjoint = false;
+  }
+  *order = disjoint ? 2 : 1;
   const size_t used = l.entries_off + sizeof(bsx::ChunkEntry) * ent.size();
   words->assign(align_up(used, 4) / 4, 0u);
   std::memcpy(words->data(), ptr.data(), l.ptr_bytes);
@@ -394,14 +408,15 @@ bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, co
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   std::vector<uint32_t> words;
-  int32_t n_entries = 0;
-  build_fwd_descriptor(chunks, &words, &n_entries);
+  int32_t n_entries = 0, entries_order = 0;
+  build_fwd_descriptor(chunks, &words, &n_entries, &entries_order);
   const FwdLayout l = fwd_layout(chunks->n_slots, chunks->n_chunks);
 
   bsx::FwdParams p{};
   hipError_t e = place_table(words, ws, s, &p.table);
   if (e != hipSuccess) return device_status(e, "forward descriptor upload");
   p.entries_off = uint32_t(l.entries_off);
+  p.entries_order = entries_order;
   p.q = q;
   p.k = k;
   p.v = v;

@@ -75,6 +75,9 @@ struct FwdParams {
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
   uint32_t entries_off;
+  // order of each slot's chunk entries: 0 any, 1 sorted by start, 2 sorted and
+  // disjoint (so their ends increase too)
+  int32_t entries_order;
   const int32_t* order;  // bf16 launch order (workgroup -> item), or null: natural order
   // split launches (order pass output, else null): piece index per workgroup, and
   // split[0] = tiles per piece P, split[4 + code] = first partial slot of item `code`

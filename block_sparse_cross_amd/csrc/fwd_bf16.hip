@@ -199,7 +199,7 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
   const int64_t prow = (int64_t(sb + pj) * ROWS + wave * 32 + col);  // split: partial row
   TileWalk walk;
   walk.seg.init(p.table.dev ? p.table.dev : (const char*)(p.table.words),
-                p.entries_off, slot, is_self, mlo, mhi);
+                p.entries_off, slot, is_self, mlo, mhi, p.entries_order);
   bool have = mlo < mhi && walk.first();
   int left = INT32_MAX;  // tiles this workgroup may still take
   if (have && sb >= 0) {

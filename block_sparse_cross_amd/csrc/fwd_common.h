@@ -102,16 +102,19 @@ struct SegmentWalk {
   int64_t minlo;
   int64_t maxhi;
   bool self_slot;
+  bool sorted;  // entries sorted by start: the walk ends at the first start >= maxhi
   int64_t seg0;
   int64_t seg1;
   int64_t local0;
 
-  // table: slot_ptr (int32) at byte 0, ChunkEntry list at entries_off
+  // table: slot_ptr (int32) at byte 0, ChunkEntry list at entries_off; order: the
+  // order of each slot's entries (0 any, 1 sorted by start, 2 sorted and disjoint)
   __device__ void init(const char* table, uint32_t entries_off, int slot, bool is_self,
-                       int64_t lo, int64_t hi) {
+                       int64_t lo, int64_t hi, int order = 0) {
     self_slot = is_self;
     minlo = lo;
     maxhi = hi;
+    sorted = order >= 1;
     if (is_self) {
       ent = nullptr;
       e = 0;
@@ -121,12 +124,29 @@ struct SegmentWalk {
       ent = reinterpret_cast<const ChunkEntry*>(table + entries_off);
       e = uniform32(slot_ptr[slot]);
       e_end = uniform32(slot_ptr[slot + 1]);
+      if (order >= 2) {
+        // disjoint entries sorted by start: their ends increase too, so the first entry
+        // that ends after minlo is found by bisection
+        int a = e, b = e_end;
+        while (a < b) {
+          const int mid = (a + b) >> 1;
+          const ChunkEntry c = ent[mid];
+          const int64_t end =
+              uniform_i64(c.start) + (int64_t(uniform32(int32_t(c.len))) & 0xffffffffll);
+          if (end > minlo)
+            b = mid;
+          else
+            a = mid + 1;
+        }
+        e = a;
+      }
     }
   }
 
   // Walks entries [e0, e1) of an explicit list (all chunks, for the backward pass).
   __device__ void init_range(const ChunkEntry* list, int e0, int e1, int64_t lo, int64_t hi) {
     self_slot = false;
+    sorted = false;
     minlo = lo;
     maxhi = hi;
     ent = list;
@@ -147,6 +167,10 @@ struct SegmentWalk {
     while (e < e_end) {
       const ChunkEntry c = ent[e++];
       const int64_t start = uniform_i64(c.start);
+      if (sorted && start >= maxhi) {  // no later entry reaches the range
+        e = e_end;
+        return false;
+      }
       const int64_t len = uniform32(int32_t(c.len)) & 0xffffffffll;
       const int64_t loff = uniform32(int32_t(c.local_off)) & 0xffffffffll;
       const int64_t a = start > minlo ? start : minlo;

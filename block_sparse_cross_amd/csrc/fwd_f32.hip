@@ -92,7 +92,7 @@ __global__ __launch_bounds__(THREADS) void fwd_f32_kernel(FwdParams, int n_tiles
 
   SegmentWalk walk;
   walk.init(p.table.dev ? p.table.dev : (const char*)(p.table.words),
-            p.entries_off, slot, is_self, mlo, mhi);
+            p.entries_off, slot, is_self, mlo, mhi, p.entries_order);
   while (mlo < mhi && walk.next()) {
     for (int64_t p0 = walk.seg0; p0 < walk.seg1; p0 += KT) {
       const int nvalid = int(walk.seg1 - p0 < KT ? walk.seg1 - p0 : KT);

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "bsx_internal.h"
@@ -27,6 +28,8 @@ namespace bsx {
 namespace {
 
 constexpr int kThreads = 1024;
+static_assert(sizeof(ChunkEntry) == 16 && offsetof(ChunkEntry, len) == 8,
+              "chunk entries are read as four words: start (two), len, local offset");
 constexpr int kKeys = 64;   // sort key: 0 = no item, else 1 + min(tiles, 62)
 constexpr int kWaves = kThreads / 64;
 constexpr int kTableLdsWords = 4096;  // chunk tables up to 16 KiB are read from LDS
@@ -85,9 +88,40 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
                      &mhi);
     }
     int64_t tiles = 0;
-    if (mlo < mhi)
-      tiles = is_self ? (mhi - mlo + kFwdKeyTile - 1) / kFwdKeyTile
-                      : walk_tiles(ent, slot_ptr[slot], slot_ptr[slot + 1], mlo, mhi, kFwdKeyTile);
+    if (mlo < mhi) {
+      if (is_self) {
+        tiles = (mhi - mlo + kFwdKeyTile - 1) / kFwdKeyTile;
+      } else if (lds_table) {
+        // the same walk, reading the LDS copy through the LDS array itself (through the
+        // generic table pointer every entry would be a flat load)
+        int e0 = int(s_table[slot]);
+        const int e1 = int(s_table[slot + 1]);
+        const uint32_t* w = s_table + p.entries_off / 4;
+        auto start_of = [&](int e) {
+          return int64_t(uint64_t(w[4 * e]) | (uint64_t(w[4 * e + 1]) << 32));
+        };
+        if (p.entries_order >= 2) {  // disjoint and sorted: bisect to the first entry ending after mlo
+          int b = e1;
+          while (e0 < b) {
+            const int mid = (e0 + b) >> 1;
+            if (start_of(mid) + int64_t(w[4 * mid + 2]) > mlo)
+              b = mid;
+            else
+              e0 = mid + 1;
+          }
+        }
+        for (int e = e0; e < e1; ++e) {
+          const int64_t start = start_of(e);
+          if (p.entries_order >= 1 && start >= mhi) break;  // sorted: no later entry reaches mhi
+          const int64_t a = start > mlo ? start : mlo;
+          const int64_t end = start + int64_t(w[4 * e + 2]);
+          const int64_t z = end < mhi ? end : mhi;
+          if (a < z) tiles += (z - a + kFwdKeyTile - 1) / kFwdKeyTile;
+        }
+      } else {
+        tiles = walk_tiles(ent, slot_ptr[slot], slot_ptr[slot + 1], mlo, mhi, kFwdKeyTile);
+      }
+    }
     work[it] = uint16_t(tiles < 0xffff ? tiles : 0xffff);
   }
   __syncthreads();
