@@ -529,6 +529,16 @@ bsx_status bsx_attn_bwd(const bsx_shape* shape, const void* q, const void* k, co
       ent.push_back(bsx::ChunkEntry{chunks->start[i], uint32_t(chunks->len[i]), uint32_t(acc)});
     acc += chunks->len[i];
   }
+  // the list stays in chunk index order (local offsets increase along it); walks over
+  // it may stop early or bisect when it also happens to be sorted by start / disjoint
+  int32_t entries_order = 2;
+  for (size_t i = 0; i + 1 < ent.size(); ++i) {
+    if (ent[i].start > ent[i + 1].start) {
+      entries_order = 0;
+      break;
+    }
+    if (ent[i].start + int64_t(ent[i].len) > ent[i + 1].start) entries_order = 1;
+  }
   std::vector<uint32_t> words(ent.size() * sizeof(bsx::ChunkEntry) / 4);
   if (!ent.empty()) std::memcpy(words.data(), ent.data(), ent.size() * sizeof(bsx::ChunkEntry));
   bsx::BwdParams p{};
@@ -561,6 +571,7 @@ bsx_status bsx_attn_bwd(const bsx_shape* shape, const void* q, const void* k, co
   p.ctx_len = shape->ctx_len;
   p.n_local = n_local;
   p.n_entries = int32_t(ent.size());
+  p.entries_order = entries_order;
   p.n_blocks = shape->n_blocks;
   p.block_size = shape->block_size;
   p.n_q_heads = shape->n_q_heads;

@@ -112,6 +112,8 @@ struct BwdParams {
   int64_t ctx_len;
   int64_t n_local;
   int32_t n_entries;
+  // the chunk list's order: 0 any, 1 sorted by start, 2 sorted and disjoint
+  int32_t entries_order;
   int32_t n_blocks;
   int32_t block_size;
   int32_t n_q_heads;

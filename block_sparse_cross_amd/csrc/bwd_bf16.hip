@@ -636,7 +636,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
     if (is_self) {
       walk.init(nullptr, 0, 0, true, mlo, mhi);
     } else {
-      walk.init_range(ent, 0, p.n_entries, mlo, mhi);
+      walk.init_range(ent, 0, p.n_entries, mlo, mhi, p.entries_order);
     }
     if (!(mlo < mhi) || !walk.next()) continue;
     int64_t p0 = walk.seg0;

@@ -124,34 +124,39 @@ struct SegmentWalk {
       ent = reinterpret_cast<const ChunkEntry*>(table + entries_off);
       e = uniform32(slot_ptr[slot]);
       e_end = uniform32(slot_ptr[slot + 1]);
-      if (order >= 2) {
-        // disjoint entries sorted by start: their ends increase too, so the first entry
-        // that ends after minlo is found by bisection
-        int a = e, b = e_end;
-        while (a < b) {
-          const int mid = (a + b) >> 1;
-          const ChunkEntry c = ent[mid];
-          const int64_t end =
-              uniform_i64(c.start) + (int64_t(uniform32(int32_t(c.len))) & 0xffffffffll);
-          if (end > minlo)
-            b = mid;
-          else
-            a = mid + 1;
-        }
-        e = a;
-      }
+      if (order >= 2) skip_to_first();
     }
   }
 
-  // Walks entries [e0, e1) of an explicit list (all chunks, for the backward pass).
-  __device__ void init_range(const ChunkEntry* list, int e0, int e1, int64_t lo, int64_t hi) {
+  // Disjoint entries sorted by start: their ends increase too, so the first entry that
+  // ends after minlo is found by bisection.
+  __device__ void skip_to_first() {
+    int a = e, b = e_end;
+    while (a < b) {
+      const int mid = (a + b) >> 1;
+      const ChunkEntry c = ent[mid];
+      const int64_t end =
+          uniform_i64(c.start) + (int64_t(uniform32(int32_t(c.len))) & 0xffffffffll);
+      if (end > minlo)
+        b = mid;
+      else
+        a = mid + 1;
+    }
+    e = a;
+  }
+
+  // Walks entries [e0, e1) of an explicit list (all chunks, for the backward pass);
+  // order as for init.
+  __device__ void init_range(const ChunkEntry* list, int e0, int e1, int64_t lo, int64_t hi,
+                             int order = 0) {
     self_slot = false;
-    sorted = false;
+    sorted = order >= 1;
     minlo = lo;
     maxhi = hi;
     ent = list;
     e = e0;
     e_end = e1;
+    if (order >= 2) skip_to_first();
   }
 
   // Advances to the next non-empty segment; false when the slot is exhausted.
