@@ -12,9 +12,11 @@
 // workgroups skip straight to writing an empty partial.  The order changes no result,
 // only the schedule.
 //
-// One workgroup of 1024 threads: per-(row tile, slot) tile counts go to LDS, then a
-// counting sort on the clamped count per XCD (one LDS histogram per wave, so atomics
-// meet only within a wave; suffix sums; scatter; equal counts keep no particular order).
+// One workgroup of 1024 threads per sorted list (one list per XCD, or one list when
+// items go round-robin over the XCDs): every workgroup counts the per-(row tile,
+// slot) tiles into LDS, then counting-sorts its list's slots on the clamped count
+// (one LDS histogram per wave, so atomics meet only within a wave; suffix sums;
+// scatter; equal counts keep no particular order).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
                                                              int n_tiles, int n_pairs, int grid) {
   const BSX_KARG FwdParams& p = kernel_arg0<FwdParams>();
   __shared__ uint16_t work[kOrderMaxItems];
-  __shared__ int32_t pos[kXcds][kKeys][kWaves];
+  __shared__ int32_t pos[1][kKeys][kWaves];
   const int tid = threadIdx.x;
   const int n_out = p.n_slots + p.has_self;
   const int G = p.n_q_heads / p.n_kv_heads;
@@ -128,6 +130,7 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
 
   const int wave = tid >> 6, lane = tid & 63;
   if (p.split) {
+    if (blockIdx.x > 0) return;  // (launched with one workgroup)
     // ---- split launch (fewer pairs than XCDs, at most kThreads items): thread c owns
     // item c = pair * n_tiles + tile.  P = max(min tiles, ceil(sum / target)); an item
     // of w > P tiles becomes ceil(w / P) pieces, each of P tiles but the last.
@@ -232,19 +235,23 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
     return 1 + (w < kKeys - 2 ? w : kKeys - 2);
   };
   static_assert(kKeys == 64, "one key per lane in the prefix pass");
-  for (int i = tid; i < kXcds * kKeys * kWaves; i += kThreads) (&pos[0][0][0])[i] = 0;
+  // workgroup `list` sorts the slots of XCD list `list` (bid % nx == list)
+  const int list = blockIdx.x;
+  if (list >= nx) return;
+  const int list_len = n_bids / nx;  // n_bids is a multiple of kXcds with per-XCD lists
+  for (int i = tid; i < kKeys * kWaves; i += kThreads) (&pos[0][0][0])[i] = 0;
   __syncthreads();
-  for (int bid = tid; bid < n_bids; bid += kThreads) {
+  for (int j = tid; j < list_len; j += kThreads) {
     int code;
-    const int key = key_of(bid, &code);
-    atomicAdd(&pos[bid % nx][key][wave], 1);
+    const int key = key_of(j * nx + list, &code);
+    atomicAdd(&pos[0][key][wave], 1);
   }
   __syncthreads();
-  if (wave < nx) {
-    const int x = wave, key = kKeys - 1 - lane;
+  if (wave == 0) {
+    const int key = kKeys - 1 - lane;
     int own = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) own += pos[x][key][w];
+    for (int w = 0; w < kWaves; ++w) own += pos[0][key][w];
     int incl = own;
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(incl, off);
@@ -253,18 +260,17 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
     int acc = incl - own;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const int c = pos[x][key][w];
-      pos[x][key][w] = acc;
+      const int c = pos[0][key][w];
+      pos[0][key][w] = acc;
       acc += c;
     }
   }
   __syncthreads();
-  for (int bid = tid; bid < n_bids; bid += kThreads) {
+  for (int j = tid; j < list_len; j += kThreads) {
     int code;
-    const int key = key_of(bid, &code);
-    const int x = bid % nx;
-    const int at = atomicAdd(&pos[x][key][wave], 1);
-    order[at * nx + x] = code;
+    const int key = key_of(j * nx + list, &code);
+    const int at = atomicAdd(&pos[0][key][wave], 1);
+    order[at * nx + list] = code;
   }
 }
 
@@ -364,7 +370,9 @@ hipError_t launch_fwd_order(const FwdParams& p, int32_t* order, hipStream_t stre
     grid = l.grid;
   }
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fwd_order_kernel, dim3(1), dim3(kThreads), 0, stream, p, order,
+  // one workgroup per sorted list: per XCD when pairs keep their XCD, else one
+  const int lists = (!p.split && n_pairs >= kXcds) ? kXcds : 1;
+  hipLaunchKernelGGL(fwd_order_kernel, dim3(lists), dim3(kThreads), 0, stream, p, order,
                      int(n_tiles), int(n_pairs), int(grid));
   return hipGetLastError();
 }
