@@ -48,7 +48,7 @@ constexpr int kOrderMaxItems = 32768;
 // split long items into pieces (about kSplitTargetPieces in all) that the piece
 // merge combines.
 constexpr int kSplitMaxItems = 1024;
-constexpr int kSplitTargetPieces = 2048;
+constexpr int kSplitTargetPieces = 1536;
 constexpr int kSplitMinPieceTiles = 16;
 
 // Forward problem as handed to the kernels.  The table holds slot_ptr[n_slots + 1]
