@@ -484,6 +484,14 @@ bsx_status bsx_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
                        "merge kernel");
 }
 
+// Key-tile flags of the backward: one int32 per 64 local keys.
+size_t bwd_seen_bytes(const bsx_chunks* chunks) {
+  int64_t n_local = 0;
+  for (int32_t i = 0; i < chunks->n_chunks; ++i)
+    if (chunks->len && chunks->len[i] > 0) n_local += chunks->len[i];
+  return sizeof(int32_t) * size_t((n_local + 63) / 64);
+}
+
 size_t bsx_bwd_workspace(const bsx_shape* shape, const bsx_chunks* chunks) {
   if (!shape || !chunks || chunks->n_chunks < 0 || shape->n_blocks < 0 || shape->block_size < 0 ||
       shape->n_q_heads < 0)
@@ -493,7 +501,8 @@ size_t bsx_bwd_workspace(const bsx_shape* shape, const bsx_chunks* chunks) {
       2 * sizeof(float) * size_t(shape->n_blocks) * shape->block_size * shape->n_q_heads, 256);
   const bsx::DqLayout l = bsx::bwd_dq_layout(shape->n_blocks, shape->block_size,
                                              shape->n_q_heads, shape->n_kv_heads);
-  return ent + delta + align_up(l.plan_bytes, 256) + align_up(l.part_bytes, 256) + 256;
+  return ent + delta + align_up(l.plan_bytes, 256) + align_up(l.part_bytes, 256) +
+         align_up(bwd_seen_bytes(chunks), 256) + 256;
 }
 
 bsx_status bsx_attn_bwd(const bsx_shape* shape, const void* q, const void* k, const void* v,
@@ -568,6 +577,9 @@ bsx_status bsx_attn_bwd(const bsx_shape* shape, const void* q, const void* k, co
   p.dq_plan = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ent_bytes + delta_bytes);
   p.dq_part = reinterpret_cast<float*>(static_cast<char*>(ws) + ent_bytes + delta_bytes +
                                        align_up(dl.plan_bytes, 256));
+  p.tile_seen = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ent_bytes + delta_bytes +
+                                           align_up(dl.plan_bytes, 256) +
+                                           align_up(dl.part_bytes, 256));
   p.ctx_len = shape->ctx_len;
   p.n_local = n_local;
   p.n_entries = int32_t(ent.size());

@@ -107,6 +107,9 @@ struct BwdParams {
   float* dk_self;
   float* dv_self;
   float* stats;               // workspace [N_q][H_q][2]: log2-domain LSE, rowsum(dO * O)
+  // workspace [ceil(n_local / 64)]: 1 when some draft block sees a key of the 64-key
+  // local tile, else 0 (written by the first backward kernel)
+  int32_t* tile_seen;
   int32_t* dq_plan;           // workspace: dQ work split (bwd_dq_layout)
   float* dq_part;             // workspace: partial dQ of split row tiles
   int64_t ctx_len;

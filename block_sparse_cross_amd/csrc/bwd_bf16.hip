@@ -40,6 +40,7 @@ namespace {
 
 constexpr int D = 128;
 constexpr int THREADS = 256;
+constexpr int KV_KEYS = 64;   // keys per dK / dV workgroup (and per flagged key tile)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // log2-domain LSE of a row; rows with no visible key get +inf so that P = 0.
@@ -48,25 +49,78 @@ __device__ inline float row_lse2(float lse) {
 }
 
 // ---------------------------------------------------------------- row statistics
-// stats[r] = (log2-domain LSE, D_r = rowsum(dO * O)) of query row r = q * H_q + h.
-__global__ __launch_bounds__(THREADS) void bwd_delta_kernel(const float* __restrict__ o,
-                                                            const uint16_t* __restrict__ d_o,
-                                                            const float* __restrict__ lse,
-                                                            float2* __restrict__ stats,
-                                                            int64_t n_rows) {
-  const int64_t row = int64_t(blockIdx.x) * (THREADS / 32) + (threadIdx.x >> 5);
-  const int c = (threadIdx.x & 31) * 4;
-  float acc = 0.f;
-  if (row < n_rows) {
-    const float4 ov = *reinterpret_cast<const float4*>(o + row * D + c);
-    const uint2 dv = *reinterpret_cast<const uint2*>(d_o + row * D + c);
-    acc = fmaf(ov.x, __uint_as_float(dv.x << 16), acc);
-    acc = fmaf(ov.y, __uint_as_float(dv.x & 0xffff0000u), acc);
-    acc = fmaf(ov.z, __uint_as_float(dv.y << 16), acc);
-    acc = fmaf(ov.w, __uint_as_float(dv.y & 0xffff0000u), acc);
+// Workgroups [0, delta_wgs): stats[r] = (log2-domain LSE, D_r = rowsum(dO * O)) of query
+// row r = q * H_q + h.  Workgroups from delta_wgs on: tile_seen[t] for the 64-key local
+// tiles t, THREADS tiles each: 1 when the context range [ctx_begin, anchor) of some
+// draft block holds the position of one of the tile's keys (a key's gradients are sums
+// over the rows that see it, so an unseen tile's dK and dV are zero).
+constexpr int kSeenLdsBlocks = 1024;  // block ranges staged in LDS per pass
+
+__global__ __launch_bounds__(THREADS) void bwd_delta_kernel(BwdParams, int64_t n_rows,
+                                                            int delta_wgs, int n_ctx_tiles) {
+  const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
+  if (int(blockIdx.x) < delta_wgs) {
+    const float* o = p.o;
+    const uint16_t* d_o = static_cast<const uint16_t*>(p.d_o);
+    const int64_t row = int64_t(blockIdx.x) * (THREADS / 32) + (threadIdx.x >> 5);
+    const int c = (threadIdx.x & 31) * 4;
+    float acc = 0.f;
+    if (row < n_rows) {
+      const float4 ov = *reinterpret_cast<const float4*>(o + row * D + c);
+      const uint2 dv = *reinterpret_cast<const uint2*>(d_o + row * D + c);
+      acc = fmaf(ov.x, __uint_as_float(dv.x << 16), acc);
+      acc = fmaf(ov.y, __uint_as_float(dv.x & 0xffff0000u), acc);
+      acc = fmaf(ov.z, __uint_as_float(dv.y << 16), acc);
+      acc = fmaf(ov.w, __uint_as_float(dv.y & 0xffff0000u), acc);
+    }
+    for (int off = 16; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if ((threadIdx.x & 31) == 0 && row < n_rows)
+      reinterpret_cast<float2*>(p.stats)[row] = make_float2(row_lse2(p.lse[row]), acc);
+    return;
   }
-  for (int off = 16; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if ((threadIdx.x & 31) == 0 && row < n_rows) stats[row] = make_float2(row_lse2(lse[row]), acc);
+  // ---- key tile flags
+  __shared__ int64_t s_lo[kSeenLdsBlocks], s_hi[kSeenLdsBlocks];
+  const int t = (int(blockIdx.x) - delta_wgs) * THREADS + int(threadIdx.x);
+  const bool own = t < n_ctx_tiles;
+  const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
+  const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table);
+  // the tile's key rows [r0, r1) cut into at most a few position segments: the first
+  // chunk holding row r0 (local offsets increase along the list) and those after it
+  const int64_t r0 = int64_t(t) * KV_KEYS;
+  const int64_t r1 = r0 + KV_KEYS < p.n_local ? r0 + KV_KEYS : p.n_local;
+  int e0 = 0;
+  if (own) {
+    int lo = 0, hi = p.n_entries - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (int64_t(ent[mid].local_off) <= r0) lo = mid; else hi = mid - 1;
+    }
+    e0 = lo;
+  }
+  bool seen = false;
+  for (int b0 = 0; b0 < p.n_blocks; b0 += kSeenLdsBlocks) {
+    const int nb = p.n_blocks - b0 < kSeenLdsBlocks ? p.n_blocks - b0 : kSeenLdsBlocks;
+    __syncthreads();  // the previous pass is done with the staged ranges
+    for (int i = threadIdx.x; i < nb; i += THREADS)
+      visible_range(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, false, b0 + i, &s_lo[i],
+                    &s_hi[i]);
+    __syncthreads();
+    if (!own || seen) continue;
+    for (int e = e0; e < p.n_entries && !seen; ++e) {
+      const int64_t off = ent[e].local_off, len = ent[e].len;
+      if (off >= r1) break;
+      const int64_t a_row = r0 > off ? r0 : off;
+      const int64_t z_row = r1 < off + len ? r1 : off + len;
+      if (a_row >= z_row) continue;
+      const int64_t a = ent[e].start + (a_row - off), z = ent[e].start + (z_row - off);
+      for (int i = 0; i < nb; ++i)
+        if (s_lo[i] < s_hi[i] && s_lo[i] < z && s_hi[i] > a) {
+          seen = true;
+          break;
+        }
+    }
+  }
+  if (own) p.tile_seen[t] = seen ? 1 : 0;
 }
 
 // ---------------------------------------------------------------- dK / dV
@@ -83,7 +137,6 @@ __global__ __launch_bounds__(THREADS) void bwd_delta_kernel(const float* __restr
 // Key positions come from a binary search of the chunk table (from an LDS copy when
 // the table is small); the prologue's barriers wait for LDS traffic only, so the K / V
 // operand loads arrive while the window of draft blocks is compacted.
-constexpr int KV_KEYS = 64;   // keys per workgroup
 constexpr int RS = 32;        // query rows per step
 constexpr int ROW_B = D * 2;  // staged Q / dO row: 16 chunks of 16 bytes
 constexpr int WIN = 128;      // draft blocks compacted per window
@@ -183,6 +236,22 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
   const int64_t krow = key0 + kk;
   const bool kvalid = krow < key_end;
   const bool pair_live = __any(kvalid);  // same in both waves of a pair
+
+  // ---- context keys no draft block sees: their dK and dV rows are zero
+  if (!is_self && p.tile_seen[t] == 0) {
+    const int64_t rows = key_end - key0 < KV_KEYS ? key_end - key0 : KV_KEYS;
+    const int c4 = (tid & 31) * 4;
+#pragma unroll
+    for (int i = 0; i < KV_KEYS / (THREADS / 32); ++i) {
+      const int r = (tid >> 5) + i * (THREADS / 32);
+      if (r < rows) {
+        const int64_t at = ((key0 + r) * Hkv + g) * D + c4;
+        *reinterpret_cast<float4*>(p.dk + at) = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(p.dv + at) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    return;
+  }
 
   // ---- the first window's block ranges start loading (raw values, used later), a
   // small chunk table goes to LDS
@@ -969,15 +1038,18 @@ DqLayout bwd_dq_layout(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   const int64_t n_q = int64_t(p.n_blocks) * p.block_size;
   const int64_t n_rows = n_q * p.n_q_heads;
-  if (n_rows > 0) {
-    const int64_t blocks = (n_rows + (THREADS / 32) - 1) / (THREADS / 32);
-    hipLaunchKernelGGL(bwd_delta_kernel, dim3(unsigned(blocks)), dim3(THREADS), 0, stream, p.o,
-                       static_cast<const uint16_t*>(p.d_o), p.lse,
-                       reinterpret_cast<float2*>(p.stats), n_rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const int64_t n_ctx_tiles = (p.n_local + KV_KEYS - 1) / KV_KEYS;
+  {
+    const int64_t delta_wgs = (n_rows + (THREADS / 32) - 1) / (THREADS / 32);
+    const int64_t seen_wgs = (n_ctx_tiles + THREADS - 1) / THREADS;
+    if (delta_wgs + seen_wgs > 0x7fffffff) return hipErrorInvalidValue;
+    if (delta_wgs + seen_wgs > 0) {
+      hipLaunchKernelGGL(bwd_delta_kernel, dim3(unsigned(delta_wgs + seen_wgs)), dim3(THREADS), 0,
+                         stream, p, n_rows, int(delta_wgs), int(n_ctx_tiles));
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
   const int self_tiles = (p.block_size + KV_KEYS - 1) / KV_KEYS;
   const int64_t kv_grid =
       (n_ctx_tiles + (p.has_self ? int64_t(p.n_blocks) * self_tiles : 0)) * p.n_kv_heads;
