@@ -138,6 +138,7 @@ __global__ __launch_bounds__(THREADS) void bwd_delta_kernel(BwdParams, int64_t n
 // the table is small); the prologue's barriers wait for LDS traffic only, so the K / V
 // operand loads arrive while the window of draft blocks is compacted.
 constexpr int RS = 32;        // query rows per step
+constexpr int DQ_LDS_ENTRIES = 256;  // chunk lists up to this long are searched in LDS by dQ
 constexpr int ROW_B = D * 2;  // staged Q / dO row: 16 chunks of 16 bytes
 constexpr int WIN = 128;      // draft blocks compacted per window
 constexpr int XP_BYTES = 2048;  // one pair's P of one step: [u][lane] x 16 bytes
@@ -589,6 +590,8 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
   __shared__ __attribute__((aligned(16))) char lds_k1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char lds_v1[TILE_BYTES];
   __shared__ int64_t red[4][4];
+  // the chunk list, when it is short: a workgroup finds where its walk starts from LDS
+  __shared__ __attribute__((aligned(16))) ChunkEntry s_ent[DQ_LDS_ENTRIES];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
@@ -599,6 +602,18 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
   const int64_t n_rows = n_q * G;
   const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
   const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table);
+  const bool lds_ent = p.n_entries <= DQ_LDS_ENTRIES;
+  static_assert(DQ_LDS_ENTRIES == THREADS, "one chunk entry per thread");
+  // this thread's entry (start, len): buffer loads (a generic-pointer load would make
+  // every later wait include it), written to LDS once Q / dO are in flight
+  int64_t my_start = 0;
+  uint32_t my_len = 0, my_loff = 0;
+  if (lds_ent) {
+    const __amdgpu_buffer_rsrc_t er = make_rsrc(ent, uint32_t(p.n_entries) * 16u);
+    my_start = __builtin_bit_cast(int64_t, __builtin_amdgcn_raw_buffer_load_b64(er, uint32_t(tid) * 16u, 0, 0));
+    my_len = __builtin_amdgcn_raw_buffer_load_b32(er, uint32_t(tid) * 16u + 8u, 0, 0);
+    my_loff = __builtin_amdgcn_raw_buffer_load_b32(er, uint32_t(tid) * 16u + 12u, 0, 0);
+  }
 
   // this workgroup's piece: key tiles [j P, j P + P) of row tile tile_id's walk
   const int32_t* plan = p.dq_plan;
@@ -621,6 +636,11 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
                              : make_float2(INFINITY, 0.f);
   const float lse2 = stat.x, dlt = stat.y;
 
+  // the context range of the lane's block (issued before the Q / dO loads, so the range
+  // reduction waits for these alone)
+  int64_t ctx_lo = 0, ctx_hi = 0;
+  if (row_ok) visible_range(p.anchor, p.ctx_begin, p.ctx_len, B, false, blk, &ctx_lo, &ctx_hi);
+
   // Q^T and dO^T fragments of this lane's row (dims 16t + 8*half .. +8)
   bf16x8 qf[8], dof[8];
   {
@@ -635,6 +655,11 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
       qf[t] = as_bf16x8(buffer_load16(qr, off + 32 * t));
       dof[t] = as_bf16x8(buffer_load16(dr, off + 32 * t));
     }
+  }
+  if (lds_ent && tid < p.n_entries) {  // published by the range barriers below
+    s_ent[tid].start = my_start;
+    s_ent[tid].len = my_len;
+    s_ent[tid].local_off = my_loff;
   }
 
   f32x16 dq[4];
@@ -665,9 +690,9 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
   // phase 0: local context chunks; phase 1: the draft blocks' own keys
   for (int phase = 0; phase < (p.has_self && pj == 0 ? 2 : 1); ++phase) {
     const bool is_self = phase == 1;
-    int64_t lo = 0, hi = 0;
-    if (row_ok)
-      visible_range(p.anchor, p.ctx_begin, p.ctx_len, B, is_self, blk, &lo, &hi);
+    int64_t lo = ctx_lo, hi = ctx_hi;
+    if (row_ok && is_self)
+      visible_range(p.anchor, p.ctx_begin, p.ctx_len, B, true, blk, &lo, &hi);
     const bool live = row_ok && lo < hi;
     {
       int64_t a = live ? lo : INT64_MAX, b = live ? hi : INT64_MIN;
@@ -680,7 +705,9 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
         c = c3 > c ? c3 : c;
         e = e2 < e ? e2 : e;
       }
-      __syncthreads();  // previous phase is done with `red` and the stages
+      // (LDS-only barriers: the Q / dO loads stay in flight while the walk starts and the
+      // first K / V tile loads; the first MFMA waits for them)
+      lds_barrier();  // previous phase is done with `red` (and the stages)
       if (lane == 0) {
         red[wave][0] = a;
         red[wave][1] = b;
@@ -688,7 +715,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
         red[wave][3] = e;
       }
     }
-    __syncthreads();
+    lds_barrier();
     int64_t mlo = INT64_MAX, mhi = INT64_MIN, lmax = INT64_MIN, hmin = INT64_MAX;
     for (int w = 0; w < 4; ++w) {
       mlo = red[w][0] < mlo ? red[w][0] : mlo;
@@ -701,17 +728,58 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
     lmax = uniform64(lmax);
     hmin = uniform64(hmin);
 
+    // the context walk of piece pj starts pj * P tiles in; the self walk is one piece.
+    // With the list in LDS the start (chunk entry, tile within its segment) is found
+    // there: bisection to the first chunk that ends after mlo when the list is sorted
+    // and disjoint, then whole chunks skipped by their tile counts.
+    int e_start = -1;
+    int64_t skip_in = 0;
+    if (!is_self && lds_ent && mlo < mhi) {
+      int e = 0;
+      if (p.entries_order >= 2) {
+        int b1 = p.n_entries;
+        while (e < b1) {
+          const int mid = (e + b1) >> 1;
+          if (s_ent[mid].start + int64_t(s_ent[mid].len) > mlo) b1 = mid; else e = mid + 1;
+        }
+      }
+      int64_t skip = int64_t(pj) * P;
+      for (; e < p.n_entries; ++e) {
+        const int64_t st = s_ent[e].start;
+        if (p.entries_order >= 1 && st >= mhi) break;
+        const int64_t a = st > mlo ? st : mlo;
+        const int64_t en = st + int64_t(s_ent[e].len);
+        const int64_t z = en < mhi ? en : mhi;
+        if (a >= z) continue;
+        const int64_t w = (z - a + KT - 1) / KT;
+        if (skip < w) {
+          e_start = e;
+          skip_in = skip;
+          break;
+        }
+        skip -= w;
+      }
+      if (e_start < 0) continue;  // the piece is past the walk's end
+    }
     SegmentWalk walk;
     if (is_self) {
       walk.init(nullptr, 0, 0, true, mlo, mhi);
+      if (!(mlo < mhi) || !walk.next()) continue;
+    } else if (e_start >= 0) {
+      // the first segment from the LDS copy; later segments come from the list itself
+      walk.init_range(ent, e_start + 1, p.n_entries, mlo, mhi, p.entries_order >= 1 ? 1 : 0);
+      const int64_t st = s_ent[e_start].start;
+      const int64_t en = st + int64_t(s_ent[e_start].len);
+      walk.seg0 = st > mlo ? st : mlo;
+      walk.seg1 = en < mhi ? en : mhi;
+      walk.local0 = int64_t(s_ent[e_start].local_off) + (walk.seg0 - st);
     } else {
       walk.init_range(ent, 0, p.n_entries, mlo, mhi, p.entries_order);
+      if (!(mlo < mhi) || !walk.next()) continue;
     }
-    if (!(mlo < mhi) || !walk.next()) continue;
-    int64_t p0 = walk.seg0;
-    // the context walk of piece pj starts pj * P tiles in; the self walk is one piece
+    int64_t p0 = walk.seg0 + skip_in * KT;
     int left = is_self ? INT32_MAX : P;
-    if (!is_self) {
+    if (!is_self && e_start < 0) {
       int64_t skip = int64_t(pj) * P;
       bool found = true;
       while (skip > 0) {

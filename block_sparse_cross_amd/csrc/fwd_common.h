@@ -95,8 +95,9 @@ __device__ inline int64_t walk_tiles(const ChunkEntry* ent, int e0, int e1, int6
 // Walks the key segments a workgroup must visit for one slot: each segment is a
 // run of positions [seg0, seg1) stored at local rows local0 .. local0 + (seg1 - seg0),
 // already cut to the union [minlo, maxhi) of the ranges its rows can see.
-struct SegmentWalk {
-  const ChunkEntry* ent;
+template <class EntPtr>
+struct SegmentWalkT {
+  EntPtr ent;  // the entry list (global memory, or an LDS copy through an LDS pointer)
   int e;
   int e_end;
   int64_t minlo;
@@ -111,12 +112,13 @@ struct SegmentWalk {
   // order of each slot's entries (0 any, 1 sorted by start, 2 sorted and disjoint)
   __device__ void init(const char* table, uint32_t entries_off, int slot, bool is_self,
                        int64_t lo, int64_t hi, int order = 0) {
+    static_assert(sizeof(EntPtr) == sizeof(const ChunkEntry*), "init takes a global table");
     self_slot = is_self;
     minlo = lo;
     maxhi = hi;
     sorted = order >= 1;
     if (is_self) {
-      ent = nullptr;
+      ent = EntPtr{};
       e = 0;
       e_end = 1;
     } else {
@@ -147,7 +149,7 @@ struct SegmentWalk {
 
   // Walks entries [e0, e1) of an explicit list (all chunks, for the backward pass);
   // order as for init.
-  __device__ void init_range(const ChunkEntry* list, int e0, int e1, int64_t lo, int64_t hi,
+  __device__ void init_range(EntPtr list, int e0, int e1, int64_t lo, int64_t hi,
                              int order = 0) {
     self_slot = false;
     sorted = order >= 1;
@@ -190,5 +192,7 @@ struct SegmentWalk {
     return false;
   }
 };
+typedef SegmentWalkT<const ChunkEntry*> SegmentWalk;
+typedef const __attribute__((address_space(3))) ChunkEntry* LdsEntPtr;
 
 }  // namespace bsx
