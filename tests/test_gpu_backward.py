@@ -70,6 +70,15 @@ CASES = {
                     list(range(0, 4096, 512)), [512] * 8),
     "mha_block5": (700, 4, 4, 5, [3, 100, 650, 699, 700, 0, 350], None, [0, 350], [350, 350]),
     "gqa2_block8": (900, 8, 4, 8, [899, 450, 10], None, [0, 300, 600], [300, 300, 300]),
+    # chunks listed out of position order: the backward walks its list unsorted
+    "unsorted_chunks": (3000, 8, 2, 16, [100, 2999, 1500, 600], None,
+                        [2000, 0, 1000], [1000, 1000, 1000]),
+    # 300 chunks (more than the 256-entry LDS copies): chunk list walked from memory
+    "many_small_chunks": (4800, 8, 2, 16, [30, 4800, 2400, 1111, 4000], None,
+                          list(range(0, 4800, 16)), [16] * 300),
+    # 64-key tiles spanning distant chunks; rows 64..127 (positions 2024..2087) are seen
+    # by no block, so their dK/dV must be exactly zero
+    "split_tiles_unseen": (3000, 8, 2, 16, [20, 2010], None, [0, 2000, 900], [40, 100, 30]),
 }
 
 
@@ -83,14 +92,49 @@ def test_backward_small_full(case):
     k_loc, v_loc = wl.kv_chunks()
     chunks = bsx.Chunks(cs, cl)
     dq, dk, dv, dks, dvs = _gpu_forward_backward(wl, k_loc, v_loc, chunks)
-    pos = np.concatenate([np.arange(s, s + c) for s, c in zip(cs, cl)])
-    kg = np.zeros((S, hk, 128), np.float32)
-    vg = np.zeros((S, hk, 128), np.float32)
-    kg[pos], vg[pos] = k_loc, v_loc
-    o, lse = oracle.attention(wl.q, kg, vg, wl.k_self, wl.v_self, wl.anchor, wl.ctx_begin, B)
+    # reference (O, LSE): every local chunk as one slot plus the draft keys, merged (the
+    # chunks need not cover the context, so no global key array is built)
+    ro, rl = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, B, np.asarray(cs), np.asarray(cl),
+                                  np.zeros(len(cs), np.int64), 1)
+    nq = wl.q.shape[0]
+    mo, ml = oracle.lse_merge(ro.reshape(2, nq * hq, -1), rl.reshape(2, nq * hq))
+    o, lse = mo.reshape(nq, hq, -1), ml.reshape(nq, hq)
     r = oracle.attention_backward(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
                                   wl.ctx_begin, B, np.asarray(cs), np.asarray(cl), wl.d_o, o, lse)
     for name, got, ref in zip(["dq", "dk", "dv", "dk_self", "dv_self"], [dq, dk, dv, dks, dvs], r):
+        _check(name, got, ref)
+
+
+def test_backward_unseen_tile_is_zero():
+    """The key tile no block sees (see the split_tiles_unseen case) comes out as exact zeros."""
+    S, hq, hk, B, an, be, cs, cl = CASES["split_tiles_unseen"]
+    wl = custom_workload(seed=13, ctx_len=S, n_q_heads=hq, n_kv_heads=hk, block_size=B,
+                         anchor=an, ctx_begin=[0] * len(an), chunk_start=cs, chunk_len=cl,
+                         backward=True)
+    k_loc, v_loc = wl.kv_chunks()
+    dq, dk, dv, dks, dvs = _gpu_forward_backward(wl, k_loc, v_loc, bsx.Chunks(cs, cl))
+    assert np.all(dk[64:128] == 0) and np.all(dv[64:128] == 0)
+    assert np.any(dk[:64] != 0) and np.any(dk[140:] != 0)
+
+
+def test_backward_overlapping_chunks_without_self():
+    """Two chunks share positions (their keys are distinct rows at the same positions): the
+    chunk list is sorted but not disjoint.  One slot holds every chunk, no self keys."""
+    cs, cl = [0, 700, 1500], [1000, 1000, 300]
+    wl = custom_workload(seed=14, ctx_len=2048, n_q_heads=8, n_kv_heads=2, block_size=16,
+                         anchor=[900, 2048, 1600, 50], ctx_begin=[0] * 4, chunk_start=cs,
+                         chunk_len=cl, backward=True)
+    k_loc, v_loc = wl.kv_chunks()
+    chunks = bsx.Chunks(cs, cl, [0, 0, 0], 1)
+    dq, dk, dv, dks, dvs = _gpu_forward_backward(wl, k_loc, v_loc, chunks, with_self=False)
+    o_p, lse_p = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                      wl.ctx_begin, 16, np.asarray(cs), np.asarray(cl), [0, 0, 0],
+                                      1, with_self=False)
+    r = oracle.attention_backward(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, 16, np.asarray(cs), np.asarray(cl), wl.d_o,
+                                  np.nan_to_num(o_p[0]), lse_p[0], with_self=False)
+    for name, got, ref in zip(["dq", "dk", "dv"], [dq, dk, dv], r[:3]):
         _check(name, got, ref)
 
 

@@ -280,6 +280,10 @@ EDGE_CASES = {
     "packed_samples": (4096, 16, 2, 16, [100, 1500, 1600, 4000, 2500], [0, 0, 1000, 2400, 2400],
                        list(range(0, 4096, 512)), [512] * 8, [0, 1, 2, 0, 1, 2, 0, 1], 3),
     "one_chunk": (1536, 8, 1, 16, [1536, 700], None, [0], [1536], None, None),
+    # one slot whose chunks are listed out of position order (each slot's list is walked
+    # in position order)
+    "unsorted_slot": (3000, 8, 2, 16, [0, 1, 777, 2999, 3000, 1999], None,
+                      [2000, 0, 1000, 2500], [500, 1000, 1000, 500], [0, 0, 0, 1], 2),
 }
 
 
@@ -312,6 +316,28 @@ def test_forward_edge_cases(case, dtype):
     uo, ul = oracle.attention(wl.q, k_glob, v_glob, wl.k_self, wl.v_self, wl.anchor,
                               wl.ctx_begin, B)
     compare_partials(mo.cpu().numpy(), ml.cpu().numpy(), uo, ul, tol_o, tol_l, "merged")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_overlapping_chunks(dtype):
+    """Chunks that share positions (distinct keys at the same positions) in one slot: the
+    slot's list is sorted but not disjoint.  Partials against the oracle's."""
+    cs, cl = [700, 0, 1500, 600], [1000, 1000, 300, 100]
+    slot_of, n_slots = [0, 0, 0, 1], 2
+    wl = custom_workload(seed=21, ctx_len=2048, n_q_heads=8, n_kv_heads=2, dtype=dtype,
+                         sigma=1.0 if dtype == "f32" else 0.5, block_size=16,
+                         anchor=[900, 2048, 1600, 50, 650], ctx_begin=[0] * 5, chunk_start=cs,
+                         chunk_len=cl)
+    k_loc, v_loc = wl.kv_chunks()
+    dev = upload(wl, k_loc, v_loc)
+    o, lse = bsx.attn_fwd(shape_of(wl), dev["q"], dev["k"], dev["v"], dev["k_self"],
+                          dev["v_self"], dev["anchor"], dev["ctx_begin"],
+                          bsx.Chunks(cs, cl, slot_of, n_slots))
+    ro, rl = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, 16, np.asarray(cs), np.asarray(cl),
+                                  np.asarray(slot_of), n_slots)
+    tol_o, tol_l = tolerances(dtype)
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_o, tol_l, "partials")
 
 
 def test_forward_rank_share_without_self_and_empty_rows():
