@@ -560,19 +560,33 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
     }
   }
 
-  if (!kvalid) return;
-  float* dst = role_b ? (is_self ? p.dk_self : p.dk) : (is_self ? p.dv_self : p.dv);
-  dst += (krow * Hkv + g) * D;
+  // ---- dV (role A) or dK (role B) of the pair's 32 keys, through LDS so that whole
+  // 512-byte rows go out per store (the accumulator holds 16 bytes of a row per lane,
+  // rows 4 KB apart).  Each wave uses one stage: row r, 16-byte chunk c at slot c ^ r,
+  // so the lane-per-row writes and the row-per-32-lanes reads are conflict-free.
+  lds_barrier();  // every wave is done with the stages
+  char* tb = reinterpret_cast<char*>(wave_u == 0 ? &stg0 : wave_u == 1 ? &stg1 : wave_u == 2 ? &stg2 : &stg3);
+  static_assert(32 * D * 4 <= int(sizeof(DkdvStage)), "a wave's rows fit one stage");
   const float sc = role_b ? p.scale : 1.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int d0 = db * 32 + 8 * a + 4 * half;
-      *reinterpret_cast<float4*>(dst + d0) =
+      const int c = 8 * db + 2 * a + half;  // dims 4c .. 4c + 3
+      *reinterpret_cast<float4*>(tb + col * (D * 4) + ((c ^ col) * 16)) =
           make_float4(acc[db][4 * a] * sc, acc[db][4 * a + 1] * sc, acc[db][4 * a + 2] * sc,
                       acc[db][4 * a + 3] * sc);
     }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in LDS
+  float* dst = role_b ? (is_self ? p.dk_self : p.dk) : (is_self ? p.dv_self : p.dv);
+  const int c = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 2 * i + (lane >> 5);
+    const float4 v = *reinterpret_cast<const float4*>(tb + r * (D * 4) + ((c ^ r) * 16));
+    const int64_t key = key0 + pair * 32 + r;
+    if (key < key_end) *reinterpret_cast<float4*>(dst + (key * Hkv + g) * D + 4 * c) = v;
+  }
 }
 
 // ---------------------------------------------------------------- dQ
