@@ -376,29 +376,45 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
     have = have_next;
   }
 
-  // ---- normalize and write this lane's half of the row
+  // ---- normalize.  The rows go out through LDS so that every store writes whole
+  // 512-byte rows (the accumulator holds 16 bytes of a row per lane): each wave puts its
+  // 32 rows in a 16 KB piece of the (now idle) stages, row r's 16-byte chunk c at slot
+  // c ^ r (conflict-free lane-per-row writes and row-per-32-lanes reads), with each
+  // row's destination next to them (-1: a row without keys, whose O is not written).
   const float ltot = lsum + __shfl_xor(lsum, 32);
-  if (!row_ok) return;
-  const bool has_keys = live && ltot > 0.f;
+  const bool has_keys = row_ok && live && ltot > 0.f;
   const float lse_out = has_keys ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
-  if (half == 0) {
+  if (row_ok && half == 0) {
     if (sb >= 0)
       p.part_lse[prow] = lse_out;
     else
       p.lse_part[orow] = lse_out;
   }
-  if (!has_keys) return;
-  const float inv = 1.f / ltot;
-  float* op = sb >= 0 ? p.part_o + prow * D : p.o_part + orow * D;
+  const float inv = has_keys ? 1.f / ltot : 0.f;
+  static_assert(4 * 32 * D * 4 + 4 * 32 * 8 <= 2 * STAGE_BYTES, "four waves' rows fit the stages");
+  char* tb = smem + wave * (32 * D * 4);
+  int64_t* s_dst = reinterpret_cast<int64_t*>(smem + 4 * 32 * D * 4) + wave * 32;
+  if (half == 0) s_dst[col] = has_keys ? (sb >= 0 ? prow : orow) * D : -1;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int d0 = db * 32 + 8 * a + 4 * half;
-      *reinterpret_cast<float4*>(op + d0) =
+      const int c = 8 * db + 2 * a + half;  // dims 4c .. 4c + 3
+      *reinterpret_cast<float4*>(tb + col * (D * 4) + ((c ^ col) * 16)) =
           make_float4(acc_o[db][4 * a] * inv, acc_o[db][4 * a + 1] * inv,
                       acc_o[db][4 * a + 2] * inv, acc_o[db][4 * a + 3] * inv);
     }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in LDS
+  float* base = sb >= 0 ? p.part_o : p.o_part;
+  const int c = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 2 * i + (lane >> 5);
+    const int64_t at = s_dst[r];
+    if (at >= 0)
+      *reinterpret_cast<float4*>(base + at + 4 * c) =
+          *reinterpret_cast<const float4*>(tb + r * (D * 4) + ((c ^ r) * 16));
+  }
 }
 
 }  // namespace
