@@ -606,6 +606,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
   __shared__ int64_t red[4][4];
   // the chunk list, when it is short: a workgroup finds where its walk starts from LDS
   __shared__ __attribute__((aligned(16))) ChunkEntry s_ent[DQ_LDS_ENTRIES];
+  __shared__ int64_t s_dst[4][32];  // destinations of the rows (epilogue)
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
@@ -908,32 +909,40 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
     }
   }
 
-  if (!row_ok) return;
-  if (split) {
-    // partial sum of piece pj, unscaled, [slot][row in tile][d]
-    float* pp = p.dq_part +
-                ((int64_t(sbase[tile_id] + pj) * Hkv + g) * QROWS + wave * 32 + col) * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = db * 32 + 8 * a + 4 * half;
-        *reinterpret_cast<float4*>(pp + d0) = make_float4(dq[db][4 * a], dq[db][4 * a + 1],
-                                                          dq[db][4 * a + 2], dq[db][4 * a + 3]);
-      }
-    return;
-  }
-  float* op = p.dq + (qi * Hq + h) * D;
-  const float sc = p.scale;
+  // ---- the rows go out through LDS so that every store writes whole 512-byte rows (the
+  // accumulator holds 16 bytes of a row per lane): wave w puts its 32 rows in tile
+  // buffer w, row r's 16-byte chunk c at slot c ^ r, with each row's destination in
+  // s_dst (-1: past the last row).  A split row tile's piece writes its unscaled
+  // partial sum, [slot][row in tile][d]; otherwise dQ = scale * sum.
+  lds_barrier();  // every wave is done with the tile buffers
+  char* tb = wave_u == 0 ? lds_k0 : wave_u == 1 ? lds_v0 : wave_u == 2 ? lds_k1 : lds_v1;
+  static_assert(32 * D * 4 <= TILE_BYTES, "a wave's rows fit one tile buffer");
+  const float sc = split ? 1.f : p.scale;
+  float* base = split ? p.dq_part : p.dq;
+  if (half == 0)
+    s_dst[wave][col] =
+        !row_ok ? -1
+                : split ? ((int64_t(sbase[tile_id] + pj) * Hkv + g) * QROWS + wave * 32 + col) * D
+                        : (qi * Hq + h) * D;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int d0 = db * 32 + 8 * a + 4 * half;
-      *reinterpret_cast<float4*>(op + d0) =
+      const int c = 8 * db + 2 * a + half;  // dims 4c .. 4c + 3
+      *reinterpret_cast<float4*>(tb + col * (D * 4) + ((c ^ col) * 16)) =
           make_float4(dq[db][4 * a] * sc, dq[db][4 * a + 1] * sc, dq[db][4 * a + 2] * sc,
                       dq[db][4 * a + 3] * sc);
     }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in LDS
+  const int c = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 2 * i + (lane >> 5);
+    const int64_t at = s_dst[wave][r];
+    if (at >= 0)
+      *reinterpret_cast<float4*>(base + at + 4 * c) =
+          *reinterpret_cast<const float4*>(tb + r * (D * 4) + ((c ^ r) * 16));
+  }
 }
 
 // ---------------------------------------------------------------- dQ split plan
