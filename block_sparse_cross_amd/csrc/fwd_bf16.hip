@@ -177,7 +177,9 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
       red[wave][3] = e;
     }
   }
-  __syncthreads();
+  // (an LDS-only barrier: the Q loads stay in flight while the walk starts and the first
+  // K / V tile loads; the first MFMA waits for them)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   int64_t mlo = INT64_MAX, mhi = INT64_MIN, lmax = INT64_MIN, hmin = INT64_MAX;
   for (int w = 0; w < 4; ++w) {
     mlo = red[w][0] < mlo ? red[w][0] : mlo;
@@ -194,8 +196,9 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
 
   // A split item's piece pj covers tiles [pj P, pj P + P) of the walk and writes a
   // normalized partial of its own (slot sb + pj of part_o / part_lse).
-  const int sb = p.split ? p.split[4 + pair * n_tiles + tile_id] : -1;
-  const int P = p.split ? p.split[0] : 0;
+  const ConstI32s split_tab = reinterpret_cast<ConstI32s>(const_bytes(p.split));  // scalar loads
+  const int sb = p.split ? split_tab[4 + pair * n_tiles + tile_id] : -1;
+  const int P = p.split ? split_tab[0] : 0;
   const int64_t prow = (int64_t(sb + pj) * ROWS + wave * 32 + col);  // split: partial row
   TileWalk walk;
   walk.seg.init(p.table.dev ? p.table.dev : (const char*)(p.table.words),

@@ -95,9 +95,19 @@ __device__ inline int64_t walk_tiles(const ChunkEntry* ent, int e0, int e1, int6
 // Walks the key segments a workgroup must visit for one slot: each segment is a
 // run of positions [seg0, seg1) stored at local rows local0 .. local0 + (seg1 - seg0),
 // already cut to the union [minlo, maxhi) of the ranges its rows can see.
-template <class EntPtr>
-struct SegmentWalkT {
-  EntPtr ent;  // the entry list (global memory, or an LDS copy through an LDS pointer)
+// The walk reads the chunk table through constant-address-space pointers: the table
+// is not written while a kernel walks it, and its entry reads (wave-uniform) become
+// scalar loads, which wait for nothing but themselves (through a generic pointer
+// they are flat loads, and waiting for one waits for every load in flight).
+typedef const __attribute__((address_space(4))) char* ConstBytes;
+typedef const __attribute__((address_space(4))) int32_t* ConstI32s;
+typedef const __attribute__((address_space(4))) ChunkEntry* ConstEntries;
+__device__ inline ConstBytes const_bytes(const void* ptr) {
+  return reinterpret_cast<ConstBytes>(reinterpret_cast<uintptr_t>(ptr));
+}
+
+struct SegmentWalk {
+  ConstEntries ent;
   int e;
   int e_end;
   int64_t minlo;
@@ -110,24 +120,30 @@ struct SegmentWalkT {
 
   // table: slot_ptr (int32) at byte 0, ChunkEntry list at entries_off; order: the
   // order of each slot's entries (0 any, 1 sorted by start, 2 sorted and disjoint)
-  __device__ void init(const char* table, uint32_t entries_off, int slot, bool is_self,
+  __device__ void init(const void* table_ptr, uint32_t entries_off, int slot, bool is_self,
                        int64_t lo, int64_t hi, int order = 0) {
-    static_assert(sizeof(EntPtr) == sizeof(const ChunkEntry*), "init takes a global table");
     self_slot = is_self;
     minlo = lo;
     maxhi = hi;
     sorted = order >= 1;
     if (is_self) {
-      ent = EntPtr{};
+      ent = nullptr;
       e = 0;
       e_end = 1;
     } else {
-      const int32_t* slot_ptr = reinterpret_cast<const int32_t*>(table);
-      ent = reinterpret_cast<const ChunkEntry*>(table + entries_off);
+      const ConstBytes table = const_bytes(table_ptr);
+      const ConstI32s slot_ptr = reinterpret_cast<ConstI32s>(table);
+      ent = reinterpret_cast<ConstEntries>(table + entries_off);
       e = uniform32(slot_ptr[slot]);
       e_end = uniform32(slot_ptr[slot + 1]);
       if (order >= 2) skip_to_first();
     }
+  }
+
+  // entry fields, wave-uniform
+  __device__ int64_t start_of(int i) const { return uniform_i64(ent[i].start); }
+  __device__ int64_t len_of(int i) const {
+    return int64_t(uniform32(int32_t(ent[i].len))) & 0xffffffffll;
   }
 
   // Disjoint entries sorted by start: their ends increase too, so the first entry that
@@ -136,10 +152,7 @@ struct SegmentWalkT {
     int a = e, b = e_end;
     while (a < b) {
       const int mid = (a + b) >> 1;
-      const ChunkEntry c = ent[mid];
-      const int64_t end =
-          uniform_i64(c.start) + (int64_t(uniform32(int32_t(c.len))) & 0xffffffffll);
-      if (end > minlo)
+      if (start_of(mid) + len_of(mid) > minlo)
         b = mid;
       else
         a = mid + 1;
@@ -149,13 +162,13 @@ struct SegmentWalkT {
 
   // Walks entries [e0, e1) of an explicit list (all chunks, for the backward pass);
   // order as for init.
-  __device__ void init_range(EntPtr list, int e0, int e1, int64_t lo, int64_t hi,
+  __device__ void init_range(const ChunkEntry* list, int e0, int e1, int64_t lo, int64_t hi,
                              int order = 0) {
     self_slot = false;
     sorted = order >= 1;
     minlo = lo;
     maxhi = hi;
-    ent = list;
+    ent = reinterpret_cast<ConstEntries>(const_bytes(list));
     e = e0;
     e_end = e1;
     if (order >= 2) skip_to_first();
@@ -172,14 +185,14 @@ struct SegmentWalkT {
       return seg0 < seg1;
     }
     while (e < e_end) {
-      const ChunkEntry c = ent[e++];
-      const int64_t start = uniform_i64(c.start);
+      const int i = e++;
+      const int64_t start = start_of(i);
       if (sorted && start >= maxhi) {  // no later entry reaches the range
         e = e_end;
         return false;
       }
-      const int64_t len = uniform32(int32_t(c.len)) & 0xffffffffll;
-      const int64_t loff = uniform32(int32_t(c.local_off)) & 0xffffffffll;
+      const int64_t len = len_of(i);
+      const int64_t loff = int64_t(uniform32(int32_t(ent[i].local_off))) & 0xffffffffll;
       const int64_t a = start > minlo ? start : minlo;
       const int64_t z = start + len < maxhi ? start + len : maxhi;
       if (a < z) {
@@ -192,7 +205,6 @@ struct SegmentWalkT {
     return false;
   }
 };
-typedef SegmentWalkT<const ChunkEntry*> SegmentWalk;
-typedef const __attribute__((address_space(3))) ChunkEntry* LdsEntPtr;
+
 
 }  // namespace bsx
