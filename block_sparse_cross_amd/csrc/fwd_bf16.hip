@@ -134,14 +134,17 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
     if (row_ok && half == 0) p.lse_part[(int64_t(slot) * n_q + qi) * p.n_q_heads + h] = -INFINITY;
     return;
   }
-  int64_t lo = 0, hi = 0;
-  if (row_ok)
-    visible_range(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, is_self, qi / p.block_size,
-                  &lo, &hi);
-  const bool live = row_ok && lo < hi;
+  // the lane's block range: the raw ctx_begin / anchor loads go out first, the Q loads
+  // next, and the range is formed after both are in flight (the scheduling barrier
+  // keeps the wait for the range from moving ahead of the Q loads)
+  const int64_t blk = qi / p.block_size;
+  int64_t raw_a = 0, raw_z = 0;
+  if (row_ok && !is_self) {
+    raw_a = p.ctx_begin[blk];
+    raw_z = p.anchor[blk];
+  }
 
-  // ---- Q^T fragments (issued first: they depend on nothing below): lane (half, col)
-  // holds dims 16t + 8*half .. +8 of its row
+  // ---- Q^T fragments: lane (half, col) holds dims 16t + 8*half .. +8 of its row
   bf16x8 qf[8];
   {
     // uniform base at the tile's first query; rows past the end read as zero
@@ -157,6 +160,19 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
       qf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 32 * t,
                                                                                0, 0));
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // visible range [lo, hi) of the lane's row (the same clamping as visible_range)
+  int64_t lo = 0, hi = 0;
+  if (row_ok) {
+    if (is_self) {
+      lo = blk * p.block_size;
+      hi = lo + p.block_size;
+    } else {
+      lo = raw_a < 0 ? 0 : (raw_a > p.ctx_len ? p.ctx_len : raw_a);
+      hi = raw_z < lo ? lo : (raw_z > p.ctx_len ? p.ctx_len : raw_z);
+    }
+  }
+  const bool live = row_ok && lo < hi;
 
   // ---- workgroup-wide union [mlo, mhi) and intersection [lmax, hmin) of live ranges
   {
