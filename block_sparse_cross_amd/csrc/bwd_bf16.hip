@@ -41,6 +41,7 @@ namespace {
 constexpr int D = 128;
 constexpr int THREADS = 256;
 constexpr int KV_KEYS = 64;   // keys per dK / dV workgroup (and per flagged key tile)
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
 // log2-domain LSE of a row; rows with no visible key get +inf so that P = 0.
@@ -49,20 +50,22 @@ __device__ inline float row_lse2(float lse) {
 }
 
 // ---------------------------------------------------------------- row statistics
-// Workgroups [0, delta_wgs): stats[r] = (log2-domain LSE, D_r = rowsum(dO * O)) of query
-// row r = q * H_q + h.  Workgroups from delta_wgs on: tile_seen[t] for the 64-key local
-// tiles t, THREADS tiles each: 1 when the context range [ctx_begin, anchor) of some
-// draft block holds the position of one of the tile's keys (a key's gradients are sums
-// over the rows that see it, so an unseen tile's dK and dV are zero).
+// Workgroups [0, seen_wgs): tile_seen[t] for the 64-key local tiles t, THREADS tiles
+// each: 1 when the context range [ctx_begin, anchor) of some draft block holds the
+// position of one of the tile's keys (a key's gradients are sums over the rows that
+// see it, so an unseen tile's dK and dV are zero).  They come first so that their
+// longer loops overlap the rest.  The other workgroups: stats[r] = (log2-domain LSE,
+// D_r = rowsum(dO * O)) of query row r = q * H_q + h.
 constexpr int kSeenLdsBlocks = 1024;  // block ranges staged in LDS per pass
 
 __global__ __launch_bounds__(THREADS) void bwd_delta_kernel(BwdParams, int64_t n_rows,
-                                                            int delta_wgs, int n_ctx_tiles) {
+                                                            int seen_wgs, int n_ctx_tiles) {
   const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
-  if (int(blockIdx.x) < delta_wgs) {
+  if (int(blockIdx.x) >= seen_wgs) {
     const float* o = p.o;
     const uint16_t* d_o = static_cast<const uint16_t*>(p.d_o);
-    const int64_t row = int64_t(blockIdx.x) * (THREADS / 32) + (threadIdx.x >> 5);
+    const int64_t row =
+        int64_t(int(blockIdx.x) - seen_wgs) * (THREADS / 32) + (threadIdx.x >> 5);
     const int c = (threadIdx.x & 31) * 4;
     float acc = 0.f;
     if (row < n_rows) {
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(THREADS) void bwd_delta_kernel(BwdParams, int64_t n
   }
   // ---- key tile flags
   __shared__ int64_t s_lo[kSeenLdsBlocks], s_hi[kSeenLdsBlocks];
-  const int t = (int(blockIdx.x) - delta_wgs) * THREADS + int(threadIdx.x);
+  const int t = int(blockIdx.x) * THREADS + int(threadIdx.x);
   const bool own = t < n_ctx_tiles;
   const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
   const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table);
@@ -247,8 +250,9 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
       const int r = (tid >> 5) + i * (THREADS / 32);
       if (r < rows) {
         const int64_t at = ((key0 + r) * Hkv + g) * D + c4;
-        *reinterpret_cast<float4*>(p.dk + at) = make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(p.dv + at) = make_float4(0.f, 0.f, 0.f, 0.f);
+        // (whole lines, written once: streamed past the caches)
+        __builtin_nontemporal_store(f32x4v{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f32x4v*>(p.dk + at));
+        __builtin_nontemporal_store(f32x4v{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f32x4v*>(p.dv + at));
       }
     }
     return;
@@ -1136,7 +1140,7 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
     if (delta_wgs + seen_wgs > 0x7fffffff) return hipErrorInvalidValue;
     if (delta_wgs + seen_wgs > 0) {
       hipLaunchKernelGGL(bwd_delta_kernel, dim3(unsigned(delta_wgs + seen_wgs)), dim3(THREADS), 0,
-                         stream, p, n_rows, int(delta_wgs), int(n_ctx_tiles));
+                         stream, p, n_rows, int(seen_wgs), int(n_ctx_tiles));
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
