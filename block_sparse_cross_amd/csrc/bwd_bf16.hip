@@ -241,21 +241,36 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
   const bool kvalid = krow < key_end;
   const bool pair_live = __any(kvalid);  // same in both waves of a pair
 
-  // ---- context keys no draft block sees: their dK and dV rows are zero
-  if (!is_self && p.tile_seen[t] == 0) {
-    const int64_t rows = key_end - key0 < KV_KEYS ? key_end - key0 : KV_KEYS;
+  // ---- context keys no draft block sees: their dK and dV rows are zero.  Tile t pairs
+  // with its mirror n - 1 - t: when exactly one of the two is seen, the seen tile's
+  // workgroup also writes the other's zero rows after its own (the unseen tiles of a
+  // packed batch cluster at the back, so their zero stores then overlap computing
+  // workgroups instead of trailing them); otherwise each unseen tile writes its own.
+  auto zero_tile = [&](int tt) {
+    const int64_t k0 = int64_t(tt) * KV_KEYS;
+    const int64_t rows = p.n_local - k0 < KV_KEYS ? p.n_local - k0 : KV_KEYS;
     const int c4 = (tid & 31) * 4;
 #pragma unroll
     for (int i = 0; i < KV_KEYS / (THREADS / 32); ++i) {
       const int r = (tid >> 5) + i * (THREADS / 32);
       if (r < rows) {
-        const int64_t at = ((key0 + r) * Hkv + g) * D + c4;
+        const int64_t at = ((k0 + r) * Hkv + g) * D + c4;
         // (whole lines, written once: streamed past the caches)
         __builtin_nontemporal_store(f32x4v{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f32x4v*>(p.dk + at));
         __builtin_nontemporal_store(f32x4v{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f32x4v*>(p.dv + at));
       }
     }
-    return;
+  };
+  bool zero_mirror = false;
+  const int t_mirror = n_ctx_tiles - 1 - t;
+  if (!is_self) {
+    const bool seen = p.tile_seen[t] != 0;
+    const bool mirror_seen = t_mirror != t && p.tile_seen[t_mirror] != 0;
+    if (!seen) {
+      if (!mirror_seen) zero_tile(t);  // else the mirror tile's workgroup writes them
+      return;
+    }
+    zero_mirror = t_mirror != t && !mirror_seen;
   }
 
   // ---- the first window's block ranges start loading (raw values, used later), a
@@ -591,6 +606,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
     const int64_t key = key0 + pair * 32 + r;
     if (key < key_end) *reinterpret_cast<float4*>(dst + (key * Hkv + g) * D + 4 * c) = v;
   }
+  if (zero_mirror) zero_tile(t_mirror);
 }
 
 // ---------------------------------------------------------------- dQ
