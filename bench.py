@@ -148,9 +148,17 @@ class Step:
 
     def prepare(self):
         """Validated, marshalled calls for the per-step launches (low host overhead)."""
-        bsx = self.bsx
-        self.cost_call = bsx.prepare_cost(self.shape, self.anchor, self.begin, self.all_chunks,
-                                          self.cost_out[1], self.cost_out[2], ws=self.cost_ws)
+        bsx, torch = self.bsx, self.torch
+        # the planning of a batch (cost kernel, cost readback, host LPT) runs on a side
+        # stream so that it overlaps the previous batch's attention on the main stream
+        self.side = torch.cuda.Stream(self.dev)
+        with torch.cuda.stream(self.side):
+            self.cost_call = bsx.prepare_cost(self.shape, self.anchor, self.begin,
+                                              self.all_chunks, self.cost_out[1], self.cost_out[2],
+                                              ws=self.cost_ws)
+        self.cost_host = torch.empty(self.cost_out[1].shape, dtype=torch.int64, pin_memory=True)
+        self.cost_ready = torch.cuda.Event()
+        self.next_chunks = None
         self.fwd_call = bsx.prepare_attn_fwd(self.shape, self.q, self.k, self.v, self.ks, self.vs,
                                              self.anchor, self.begin, self.plan0.chunks,
                                              self.o_part, self.lse_part, self.fwd_ws)
@@ -163,23 +171,31 @@ class Step:
                                                  self.bwd_ws)
 
     def plan(self):
-        """Cost kernel, then (planned workloads) readback of chunk costs and LPT."""
-        c = self.cfg
+        """Plans one batch: the cost kernel on the side stream, then (planned workloads)
+        readback of the chunk costs into pinned memory and the host LPT.  Returns the
+        batch's chunk table (None: the table does not depend on the costs)."""
+        c, torch = self.cfg, self.torch
         self.cost_call()
         if c.slot_mode == "per_chunk":
-            return  # one partial per chunk: the plan does not depend on the costs
-        cost_host = self.cost_out[1].cpu().numpy()
-        r = self.bsx.lpt(cost_host, c.n_bins)
+            return None  # one partial per chunk: the plan does not depend on the costs
+        with torch.cuda.stream(self.side):
+            self.cost_host.copy_(self.cost_out[1], non_blocking=True)
+            self.cost_ready.record(self.side)
+        self.cost_ready.synchronize()
+        r = self.bsx.lpt(self.cost_host.numpy(), c.n_bins)
         wl = self.wl
         if c.slot_mode == "lpt":
-            chunks = self.bsx.Chunks(wl.chunk_start, wl.chunk_len, r.bin_of, c.n_bins)
-        else:
-            rank = int(np.argmax(r.loads))
-            mine = np.nonzero(r.bin_of == rank)[0]
-            if not np.array_equal(mine, self.plan0.local_chunks):
-                raise RuntimeError("plan changed between steps")
-            chunks = self.bsx.Chunks(wl.chunk_start[mine], wl.chunk_len[mine],
-                                     np.zeros(len(mine), np.int32), 1)
+            return self.bsx.Chunks(wl.chunk_start, wl.chunk_len, r.bin_of, c.n_bins)
+        rank = int(np.argmax(r.loads))
+        mine = np.nonzero(r.bin_of == rank)[0]
+        if not np.array_equal(mine, self.plan0.local_chunks):
+            raise RuntimeError("plan changed between steps")
+        return self.bsx.Chunks(wl.chunk_start[mine], wl.chunk_len[mine],
+                               np.zeros(len(mine), np.int32), 1)
+
+    def use(self, chunks):
+        if chunks is None:
+            return
         self.fwd_call.set_chunks(chunks, self.plan0.chunks)
         if self.bwd_call is not None:
             self.bwd_call.set_chunks(chunks, self.plan0.chunks)
@@ -191,11 +207,17 @@ class Step:
         self.merge_call()
 
     def run(self):
-        self.plan()
+        """One step: the batch's attention (forward, merge, backward) with the plan made
+        for it, then the next batch's plan while that work runs on the GPU.  The first
+        call plans its own batch first."""
+        if self.next_chunks is None:
+            self.next_chunks = (self.plan(),)
+        self.use(self.next_chunks[0])
         self.fwd_call()
         self.merge_call()
         if self.bwd_call is not None:
             self.bwd_call()
+        self.next_chunks = (self.plan(),)
 
 
 def time_forward(step: Step, reps: int):
