@@ -12,7 +12,7 @@ import block_sparse_cross_amd as bsx
 import oracle
 from block_sparse_cross_amd._lib import (BSX_E_INVALID, BSX_E_UNSUPPORTED, BSX_E_WORKSPACE,
                                          BsxChunks, BsxShape, lib)
-from workloads import CONFIGS, make_workload
+from workloads import get_config, make_workload
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "bsx.h")
 
@@ -38,9 +38,9 @@ def test_status_strings():
     assert L.bsx_status_string(3) == b"BSX_E_WORKSPACE"
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4])
-def test_lpt_matches_oracle_on_workload_costs(idx):
-    wl = make_workload(CONFIGS[idx])
+@pytest.mark.parametrize("name", ["b27_s64k", "rank_p64_s1m", "train_pack128k"])
+def test_lpt_matches_oracle_on_workload_costs(name):
+    wl = make_workload(get_config(name))
     _, cost = oracle.chunk_costs(wl.anchor, wl.ctx_begin, wl.cfg.block_size, wl.chunk_start,
                                  wl.chunk_len)
     got = bsx.lpt(cost, wl.cfg.n_bins)
@@ -182,9 +182,9 @@ def test_place_matches_oracle_random(mode, seed):
     assert got.imbalance == pytest.approx(imb, rel=1e-12, abs=1e-15)
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4])
-def test_place_matches_oracle_on_workload_costs(idx):
-    wl = make_workload(CONFIGS[idx])
+@pytest.mark.parametrize("name", ["b27_s64k", "rank_p64_s1m", "train_pack128k"])
+def test_place_matches_oracle_on_workload_costs(name):
+    wl = make_workload(get_config(name))
     _, cost = oracle.chunk_costs(wl.anchor, wl.ctx_begin, wl.cfg.block_size, wl.chunk_start,
                                  wl.chunk_len)
     for mode, fn in [("contiguous", oracle.contiguous), ("zigzag", oracle.zigzag),

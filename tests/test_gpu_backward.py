@@ -13,7 +13,7 @@ import torch
 import block_sparse_cross_amd as bsx
 import oracle
 from parity_helpers import log, shape_of, upload
-from workloads import CONFIGS, make_workload
+from workloads import get_config, make_workload
 from workloads.gen import custom_workload
 
 pytestmark = pytest.mark.gpu
@@ -164,7 +164,7 @@ def test_backward_rank_share_without_self():
 def test_backward_training_workload_one_kv_head():
     """The full-size training step (8 packed samples, 131072 keys, 16 LPT bins); the oracle
     computes every gradient of one KV head (all its query heads, keys and draft keys)."""
-    wl = make_workload(CONFIGS[4])
+    wl = make_workload(get_config("train_pack128k"))
     c = wl.cfg
     log(f"backward, {c.name}: blocks={wl.n_blocks}")
     k_loc, v_loc = wl.kv_chunks()

@@ -18,7 +18,7 @@ import oracle
 from block_sparse_cross_amd.pipeline import make_plan
 from parity_helpers import (compare_partials, log, oracle_plan, sample_pairs, shape_of,
                             tolerances, upload)
-from workloads import CONFIGS, get_config, make_workload
+from workloads import get_config, make_workload
 from workloads.gen import custom_workload, draw_merge_sets
 
 pytestmark = pytest.mark.gpu
@@ -35,9 +35,9 @@ def _device():
 
 # ----------------------------------------------------------------------------- cost + LPT
 
-@pytest.mark.parametrize("idx", range(5))
-def test_cost_kernel_bit_exact(idx):
-    wl = make_workload(CONFIGS[idx])
+@pytest.mark.parametrize("name", ["tiny_f32", "a3b_s16k", "b27_s64k", "rank_p64_s1m", "train_pack128k"])
+def test_cost_kernel_bit_exact(name):
+    wl = make_workload(get_config(name))
     log(f"cost kernel, workload {wl.cfg.name}: blocks={wl.n_blocks} chunks={wl.n_chunks}")
     shape = shape_of(wl)
     anchor = torch.from_numpy(wl.anchor).cuda()
@@ -78,9 +78,9 @@ def test_cost_kernel_ragged_chunks_and_bad_mask():
     assert int(err.item()) == 1
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4])
-def test_plan_matches_oracle(idx):
-    wl = make_workload(CONFIGS[idx])
+@pytest.mark.parametrize("name", ["b27_s64k", "rank_p64_s1m", "train_pack128k"])
+def test_plan_matches_oracle(name):
+    wl = make_workload(get_config(name))
     c = wl.cfg
     ref = oracle_plan(wl)
     plan = make_plan(shape_of(wl), wl.chunk_start, wl.chunk_len, c.slot_mode, c.n_bins,
@@ -130,7 +130,7 @@ def _oracle_partials(wl, k_loc, v_loc, starts, lens, slot_of, n_slots, with_self
 
 
 def test_forward_f32_tiny_full():
-    wl = make_workload(CONFIGS[0])
+    wl = make_workload(get_config("tiny_f32"))
     log(f"forward f32, {wl.cfg.name}")
     ref = oracle_plan(wl)
     dev, k_loc, v_loc, starts, lens, o, lse = _run_forward(wl, ref)
@@ -144,7 +144,7 @@ def test_forward_f32_tiny_full():
 
 
 def test_forward_bf16_a3b_full():
-    wl = make_workload(CONFIGS[1])
+    wl = make_workload(get_config("a3b_s16k"))
     log(f"forward bf16, {wl.cfg.name} (all rows)")
     ref = oracle_plan(wl)
     dev, k_loc, v_loc, starts, lens, o, lse = _run_forward(wl, ref)
@@ -161,13 +161,13 @@ def test_forward_bf16_a3b_full():
     compare_partials(mo.cpu().numpy(), ml.cpu().numpy(), uo, ul, tol_o, tol_l, "merged")
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4])
-def test_forward_bf16_full_size_sampled(idx):
-    wl = make_workload(CONFIGS[idx])
+@pytest.mark.parametrize("name,seed", [("b27_s64k", 2), ("rank_p64_s1m", 3), ("train_pack128k", 4)])
+def test_forward_bf16_full_size_sampled(name, seed):
+    wl = make_workload(get_config(name))
     log(f"forward bf16, {wl.cfg.name} (sampled block/head pairs)")
     ref = oracle_plan(wl)
     dev, k_loc, v_loc, starts, lens, o, lse = _run_forward(wl, ref)
-    pairs = sample_pairs(wl, 6, seed=idx)
+    pairs = sample_pairs(wl, 6, seed=seed)
     ro, rl = _oracle_partials(wl, k_loc, v_loc, starts, lens, ref["slot_of"], ref["n_slots"],
                               wl.cfg.self_slot, pairs)
     tol_o, tol_l = tolerances("bf16")
@@ -361,7 +361,7 @@ def test_forward_rank_share_without_self_and_empty_rows():
 def test_forward_sharp_scores():
     """The a3b shape with Q scaled by 4 (exact in bf16): score spread ~4x, so the online
     softmax rescaling is exercised far from the near-uniform regime."""
-    wl = make_workload(CONFIGS[1])
+    wl = make_workload(get_config("a3b_s16k"))
     wl.q = wl.q * 4.0
     ref = oracle_plan(wl)
     dev, k_loc, v_loc, starts, lens, o, lse = _run_forward(wl, ref)
@@ -391,7 +391,7 @@ def test_forward_custom_scale():
 
 def test_merge_rank_sets_full_size_sampled():
     """64 seeded partial sets of [2048, 32, 128] (one rank's view at CP size 64)."""
-    cfg = CONFIGS[3]
+    cfg = get_config("rank_p64_s1m")
     n_rows = 2048 * 32
     log("merge, 64 seeded sets of [2048, 32, 128]")
     o_sets, l_sets = draw_merge_sets(cfg, cfg.n_merge_sets, n_rows, 128)
