@@ -5,8 +5,11 @@
 One step is one pass of the whole hot path over one batch of synthetic inputs that
 are already resident in HBM: the per-chunk cost kernel, the LPT plan (host, after
 the one readback of chunk costs) for planned workloads, the forward partials, the
-exact LSE merge, and for the training workload the backward pass.  The default
-workload is the Qwen3.5-35B-A3B-drafter shape (S = 16384, H_q = 32, H_kv = 4,
+exact LSE merge, and for the training workload the backward pass.  Steps are
+pipelined as a training loop runs them: each batch is planned (cost kernel and cost
+readback on a second stream, then the host LPT) while the previous batch's attention
+runs, so every timed step does one whole plan and one whole attention pass.  The
+default workload is the Qwen3.5-35B-A3B-drafter shape (S = 16384, H_q = 32, H_kv = 4,
 d = 128, 32 anchors x 16 draft queries, 16 KV chunks of 1024 with one partial per
 chunk plus the draft block's own keys).
 
