@@ -422,7 +422,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU Split-KV exchange is not part of this build)", file=sys.stderr)
+              "(the multi-GPU Split-KV exchange is not implemented here)", file=sys.stderr)
         sys.exit(2)
     import torch
 
