@@ -50,6 +50,8 @@ def parse():
                     help="event-timed launches of the forward kernel for the roofline")
     ap.add_argument("--sweep", action="store_true",
                     help="print the fixed-query-budget context sweep (S = 16K .. 1M) and exit")
+    ap.add_argument("--cost-stress", action="store_true",
+                    help="time the cost kernel at 65536 blocks x 4096 chunks and exit")
     ap.add_argument("--planners", action="store_true",
                     help="print the chunk-placement comparison (imbalance, host us) and exit")
     ap.add_argument("--no-merge-bench", action="store_true",
@@ -386,6 +388,46 @@ def context_sweep(device, steps: int = 20, warmup: int = 3):
     return rows
 
 
+def cost_stress(device, reps: int = 20):
+    """Cost kernel at a write-bound size: 65536 draft blocks x 4096 chunks of 1024 keys
+    (2 GiB of int64 counts).  Algorithmic bytes: block ranges and chunk table read,
+    counts and chunk costs written."""
+    import torch
+
+    import block_sparse_cross_amd as bsx
+
+    nb, nc, L = 65536, 4096, 1024
+    S = nc * L
+    rng = np.random.default_rng(23)
+    anchor = rng.integers(0, S + 1, size=nb)
+    begin = np.minimum(anchor, rng.integers(0, S + 1, size=nb))
+    shape = bsx.Shape(n_blocks=nb, block_size=16, n_q_heads=32, n_kv_heads=4, ctx_len=S)
+    chunks = bsx.Chunks(np.arange(nc) * L, np.full(nc, L))
+    an = torch.from_numpy(anchor).to(device)
+    be = torch.from_numpy(begin).to(device)
+    counts = torch.empty((nb, nc), dtype=torch.int64, device=device)
+    cost = torch.empty(nc, dtype=torch.int64, device=device)
+    err = torch.empty(1, dtype=torch.int32, device=device)
+    ws = torch.empty(max(bsx.cost_workspace_bytes(nc), 256), dtype=torch.uint8, device=device)
+    call = bsx.prepare_cost(shape, an, be, chunks, cost, err, counts=counts, ws=ws)
+    for _ in range(3):
+        call()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = 16 * nb + 16 * nc + 8 * nb * nc + 8 * nc + 4
+    return {"n_blocks": nb, "n_chunks": nc, "chunk_len": L, "launch_us": round(us, 2),
+            "bytes_per_launch": nbytes, "achieved_GBs": round(nbytes / us / 1e3, 1),
+            "peak_GBs": PEAK_HBM_GBS, "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+            "mask_err": int(err.item())}
+
+
 def planner_comparison(device, reps: int = 200):
     """Chunk placements on the planned workloads' realized costs (cost kernel on the GPU):
     imbalance and host time per plan for LPT and the static layouts the pages compare."""
@@ -435,6 +477,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.sweep:
         print(json.dumps({"sweep": context_sweep(dev)}), flush=True)
+        return
+    if args.cost_stress:
+        print(json.dumps({"cost_stress": cost_stress(dev)}), flush=True)
         return
     if args.planners:
         print(json.dumps({"planners": planner_comparison(dev),

@@ -295,8 +295,17 @@ bsx_status bsx_place(int32_t mode, int32_t n_items, const int64_t* cost, int32_t
   return ok();
 }
 
-size_t bsx_cost_workspace(int32_t n_chunks) {
+// Cost workspace: the chunk table (when it is not inline), then for launches over many
+// blocks the block groups' chunk sums and mask flags.
+static size_t cost_table_bytes(int32_t n_chunks) {
   return align_up(sizeof(bsx::ChunkEntry) * size_t(n_chunks < 0 ? 0 : n_chunks), 256) + 256;
+}
+
+size_t bsx_cost_workspace(int32_t n_chunks) {
+  const size_t nc = size_t(n_chunks < 0 ? 0 : n_chunks);
+  const size_t groups = size_t(bsx::cost_max_groups(n_chunks < 0 ? 0 : n_chunks));
+  return cost_table_bytes(n_chunks) + align_up(sizeof(int64_t) * groups * nc, 256) +
+         align_up(sizeof(int32_t) * groups, 256);
 }
 
 bsx_status bsx_cost(const bsx_shape* shape, const int64_t* anchor, const int64_t* ctx_begin,
@@ -331,6 +340,21 @@ bsx_status bsx_cost(const bsx_shape* shape, const int64_t* anchor, const int64_t
   p.n_blocks = shape->n_blocks;
   p.block_size = shape->block_size;
   p.n_chunks = chunks->n_chunks;
+  // enough block groups to fill the chip, each a whole number of 256-block rounds
+  const int32_t rounds = (shape->n_blocks + 255) / 256;
+  const int32_t max_groups = bsx::cost_max_groups(chunks->n_chunks);
+  const int32_t want = rounds < max_groups ? rounds : max_groups;
+  p.span = shape->n_blocks > 0 ? shape->n_blocks : 1;
+  p.part = nullptr;
+  p.bad = nullptr;
+  if (want > 1) {
+    const int32_t per = (rounds + want - 1) / want;  // rounds per group
+    p.span = per * 256;
+    char* base = static_cast<char*>(ws) + cost_table_bytes(chunks->n_chunks);
+    p.part = reinterpret_cast<int64_t*>(base);
+    p.bad = reinterpret_cast<int32_t*>(
+        base + align_up(sizeof(int64_t) * size_t(max_groups) * size_t(chunks->n_chunks), 256));
+  }
   return device_status(bsx::launch_cost(p, s), "cost kernel");
 }
 

@@ -138,7 +138,20 @@ struct CostParams {
   int32_t block_size;
   int32_t n_chunks;
   ChunkTable table;         // ChunkEntry per chunk, every chunk, in index order
+  // Launches with many blocks split them into groups of `span` blocks (gridDim.y groups):
+  // each group writes its chunk sums to part[group][n_chunks] and its mask flag to
+  // bad[group], and a second pass adds them.  Null when one group covers every block.
+  int64_t* part;
+  int32_t* bad;
+  int32_t span;
 };
+// Workgroups the cost launch aims for when it splits the blocks into groups.
+constexpr int kCostTargetWgs = 2048;
+// Most block groups a launch over n_chunks chunks uses (sizes its workspace).
+inline int32_t cost_max_groups(int32_t n_chunks) {
+  const int32_t n_cg = n_chunks > 64 ? (n_chunks + 63) / 64 : 1;
+  return (kCostTargetWgs + n_cg - 1) / n_cg;
+}
 
 // Largest payload one upload launch carries in its kernel arguments.
 constexpr int kUploadWords = kInlineBytes / 4;

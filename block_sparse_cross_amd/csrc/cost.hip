@@ -32,11 +32,14 @@ __global__ __launch_bounds__(kThreads) void cost_kernel(CostParams p) {
     c0 = ce.start;
     c1 = c0 + ce.len;
   }
+  // this workgroup's blocks: group blockIdx.y of `span` blocks
+  const int b_begin = int(blockIdx.y) * p.span;
+  const int b_end = p.n_blocks - b_begin < p.span ? p.n_blocks : b_begin + p.span;
   int bad = 0;
   int64_t total = 0;
-  for (int b0 = 0; b0 < p.n_blocks; b0 += kThreads) {
+  for (int b0 = b_begin; b0 < b_end; b0 += kThreads) {
     const int b = b0 + tid;
-    if (b < p.n_blocks) {
+    if (b < b_end) {
       int64_t lo = p.ctx_begin[b], hi = p.anchor[b];
       bad |= (lo < 0) | (lo > hi) | (hi > p.ctx_len);
       lo = lo < 0 ? 0 : (lo > p.ctx_len ? p.ctx_len : lo);
@@ -45,28 +48,54 @@ __global__ __launch_bounds__(kThreads) void cost_kernel(CostParams p) {
       s_hi[tid] = hi;
     }
     __syncthreads();
-    const int nb = p.n_blocks - b0 < kThreads ? p.n_blocks - b0 : kThreads;
+    const int nb = b_end - b0 < kThreads ? b_end - b0 : kThreads;
     for (int i = wave; i < nb; i += 4) {
       const int64_t a = s_lo[i] > c0 ? s_lo[i] : c0;
       const int64_t z = s_hi[i] < c1 ? s_hi[i] : c1;
       const int64_t n = z > a ? (z - a) * p.block_size : 0;
-      if (c_ok && p.counts) p.counts[int64_t(b0 + i) * p.n_chunks + c] = n;
+      // counts are written once and not read back here: non-temporal stores
+      if (c_ok && p.counts) __builtin_nontemporal_store(n, p.counts + int64_t(b0 + i) * p.n_chunks + c);
       total += n;
     }
     __syncthreads();
   }
   s_part[wave][lane] = total;
   bad = __syncthreads_or(bad);
-  if (blockIdx.x == 0 && tid == 0) *p.mask_err = bad ? 1 : 0;
-  if (wave == 0 && c_ok)
-    p.chunk_cost[c] = s_part[0][lane] + s_part[1][lane] + s_part[2][lane] + s_part[3][lane];
+  const int64_t sum = s_part[0][lane] + s_part[1][lane] + s_part[2][lane] + s_part[3][lane];
+  if (!p.part) {
+    if (blockIdx.x == 0 && tid == 0) *p.mask_err = bad ? 1 : 0;
+    if (wave == 0 && c_ok) p.chunk_cost[c] = sum;
+  } else {
+    if (blockIdx.x == 0 && tid == 0) p.bad[blockIdx.y] = bad;
+    if (wave == 0 && c_ok) p.part[int64_t(blockIdx.y) * p.n_chunks + c] = sum;
+  }
+}
+
+// Adds the block groups' chunk sums (exact integer sums) and their mask flags.
+__global__ __launch_bounds__(kThreads) void cost_sum_kernel(CostParams p, int n_groups) {
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  if (c < p.n_chunks) {
+    int64_t t = 0;
+    for (int g = 0; g < n_groups; ++g) t += p.part[int64_t(g) * p.n_chunks + c];
+    p.chunk_cost[c] = t;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    int any = 0;
+    for (int g = 0; g < n_groups; ++g) any |= p.bad[g];
+    *p.mask_err = any ? 1 : 0;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_cost(const CostParams& p, hipStream_t stream) {
   const int blocks = p.n_chunks > 0 ? (p.n_chunks + kChunksPerWg - 1) / kChunksPerWg : 1;
-  hipLaunchKernelGGL(cost_kernel, dim3(blocks), dim3(kThreads), 0, stream, p);
+  const int groups = p.part ? (p.n_blocks + p.span - 1) / p.span : 1;
+  hipLaunchKernelGGL(cost_kernel, dim3(blocks, groups), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !p.part) return e;
+  const int sum_blocks = p.n_chunks > 0 ? (p.n_chunks + kThreads - 1) / kThreads : 1;
+  hipLaunchKernelGGL(cost_sum_kernel, dim3(sum_blocks), dim3(kThreads), 0, stream, p, groups);
   return hipGetLastError();
 }
 

@@ -52,6 +52,28 @@ def test_cost_kernel_bit_exact(name):
     assert torch.equal(counts, counts2) and torch.equal(cost, cost2)
 
 
+def test_cost_kernel_stress_size_sampled():
+    # 65536 blocks x 4096 chunks of 1024 keys (2 GiB of counts): sampled rows against the
+    # oracle; every row and the chunk costs against properties that hold at any size
+    nb, nc, L = 65536, 4096, 1024
+    S = nc * L
+    rng = np.random.default_rng(23)
+    anchor = rng.integers(0, S + 1, size=nb)
+    begin = np.minimum(anchor, rng.integers(0, S + 1, size=nb))
+    log(f"cost kernel, {nb} blocks x {nc} chunks")
+    shape = bsx.Shape(n_blocks=nb, block_size=16, n_q_heads=32, n_kv_heads=4, ctx_len=S)
+    starts, lens = np.arange(nc) * L, np.full(nc, L)
+    counts, cost, err = bsx.cost(shape, torch.from_numpy(anchor).cuda(),
+                                 torch.from_numpy(begin).cuda(), bsx.Chunks(starts, lens))
+    assert int(err.item()) == 0
+    sel = np.sort(rng.choice(nb, 8, replace=False))
+    ref, _ = oracle.chunk_costs(anchor[sel], begin[sel], 16, starts, lens)
+    assert np.array_equal(counts[torch.from_numpy(sel).cuda()].cpu().numpy(), ref)
+    # each block's row sums to B times its visible length; chunk costs are column sums
+    assert torch.equal(counts.sum(1).cpu(), torch.from_numpy(16 * (anchor - begin)))
+    assert torch.equal(counts.sum(0), cost)
+
+
 def test_cost_kernel_ragged_chunks_and_bad_mask():
     rng = np.random.default_rng(17)
     S = 5000
