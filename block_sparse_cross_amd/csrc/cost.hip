@@ -10,6 +10,10 @@
 // are written with coalesced stores; the four partial chunk sums meet in LDS, so
 // chunk_cost needs no atomics.  Workgroup 0 also checks every block's range and
 // writes mask_err (0 or 1) itself, so the flag needs no clearing beforehand.
+// Launches over many blocks split them into groups along the grid's second
+// dimension (otherwise a few thousand chunks would give only tens of workgroups);
+// each group leaves its chunk sums and flag in the workspace and a small second pass
+// adds them.
 #include <hip/hip_runtime.h>
 
 #include "bsx_internal.h"
