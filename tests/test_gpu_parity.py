@@ -74,6 +74,30 @@ def test_cost_kernel_stress_size_sampled():
     assert torch.equal(counts.sum(0), cost)
 
 
+def test_cost_kernel_block_groups_full_parity_and_flag():
+    # 600 blocks: three groups of 256 blocks, ragged chunks; every count against the
+    # oracle, then a bad range in the last group must still raise the flag
+    rng = np.random.default_rng(29)
+    S, nb = 9000, 600
+    cuts = np.sort(rng.integers(0, S + 1, size=70))
+    bounds = np.concatenate([[0], cuts, [S]])
+    starts, lens = bounds[:-1], np.diff(bounds)
+    hi = rng.integers(0, S + 1, size=nb)
+    lo = np.minimum(hi, rng.integers(0, S + 1, size=nb))
+    log(f"cost kernel, {nb} blocks in groups, {len(starts)} ragged chunks")
+    shape = bsx.Shape(n_blocks=nb, block_size=5, n_q_heads=4, n_kv_heads=2, ctx_len=S)
+    counts, cost, err = bsx.cost(shape, torch.from_numpy(hi).cuda(), torch.from_numpy(lo).cuda(),
+                                 bsx.Chunks(starts, lens))
+    rc, rcost = oracle.chunk_costs(hi, lo, 5, starts, lens)
+    assert np.array_equal(counts.cpu().numpy(), rc) and np.array_equal(cost.cpu().numpy(), rcost)
+    assert int(err.item()) == 0
+    bad_hi = hi.copy()
+    bad_hi[590] = S + 1
+    _, _, err = bsx.cost(shape, torch.from_numpy(bad_hi).cuda(), torch.from_numpy(lo).cuda(),
+                         bsx.Chunks(starts, lens))
+    assert int(err.item()) == 1
+
+
 def test_cost_kernel_ragged_chunks_and_bad_mask():
     rng = np.random.default_rng(17)
     S = 5000
