@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(PKG, "libbsx.so")
 
 SOURCES = [
     "api.cpp",
+    "layout.cpp",
     "upload.hip",
     "cost.hip",
     "lse_merge.hip",

@@ -610,7 +610,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
 }
 
 // ---------------------------------------------------------------- dQ
-constexpr int QROWS = 128;
+constexpr int QROWS = kDqRows;
 constexpr int KT = 64;
 constexpr int ROW_BYTES = D * 2;         // staged K / V row: 16 chunks of 16 bytes
 constexpr int TILE_BYTES = KT * ROW_BYTES;
@@ -1132,19 +1132,6 @@ __global__ __launch_bounds__(THREADS) void bwd_dq_reduce_kernel(BwdParams, int n
 
 }  // namespace
 
-DqLayout bwd_dq_layout(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
-                       int32_t n_kv_heads) {
-  DqLayout l{};
-  if (n_kv_heads < 1 || n_blocks < 1 || block_size < 1) return l;
-  const int64_t n_rows = int64_t(n_blocks) * block_size * (n_q_heads / n_kv_heads);
-  const int64_t target = (kDqTargetWgs + n_kv_heads - 1) / n_kv_heads;
-  l.n_tiles = (n_rows + QROWS - 1) / QROWS;
-  l.cap = target + l.n_tiles;
-  l.part_slots = 2 * target < l.cap ? 2 * target : l.cap;
-  l.plan_bytes = sizeof(int32_t) * size_t(4 + 3 * l.n_tiles + 2 * l.cap);
-  l.part_bytes = sizeof(float) * size_t(l.part_slots) * n_kv_heads * QROWS * D;
-  return l;
-}
 
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   const int64_t n_q = int64_t(p.n_blocks) * p.block_size;

@@ -438,15 +438,6 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
 
 }  // namespace
 
-int64_t fwd_bf16_grid(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
-                      int32_t n_kv_heads, int32_t n_out) {
-  const int64_t n_rows = int64_t(n_blocks) * block_size * (n_q_heads / n_kv_heads);
-  const int64_t n_tiles = (n_rows + ROWS - 1) / ROWS;
-  const int64_t n_pairs = int64_t(n_kv_heads) * n_out;
-  if (n_pairs < kXcds) return n_pairs * n_tiles;  // round-robin over XCDs
-  const int64_t per_xcd = (n_pairs + kXcds - 1) / kXcds;
-  return kXcds * per_xcd * n_tiles;
-}
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const int G = p.n_q_heads / p.n_kv_heads;

@@ -41,6 +41,9 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
                                                              int n_tiles, int n_pairs, int grid) {
   const BSX_KARG FwdParams& p = kernel_arg0<FwdParams>();
   __shared__ uint16_t work[kOrderMaxItems];
+  // exact tile counts of split launches (at most kSplitMaxItems items): pieces are cut
+  // from these, so they must not saturate like the 16-bit sort keys above
+  __shared__ int32_t work_exact[kSplitMaxItems];
   __shared__ int32_t pos[1][kKeys][kWaves];
   const int tid = threadIdx.x;
   const int n_out = p.n_slots + p.has_self;
@@ -125,6 +128,8 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
       }
     }
     work[it] = uint16_t(tiles < 0xffff ? tiles : 0xffff);
+    // a local buffer below 2^32 keys has below 2^26 tiles: the count fits int32
+    if (p.split && it < kSplitMaxItems) work_exact[it] = int32_t(tiles);
   }
   __syncthreads();
 
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
     const int n_codes = n_pairs * n_tiles;
     const int c = tid;
     int w = 0;
-    if (c < n_codes) w = work[(c % n_tiles) * n_out + (c / n_tiles) / p.n_kv_heads];
+    if (c < n_codes) w = work_exact[(c % n_tiles) * n_out + (c / n_tiles) / p.n_kv_heads];
     s_sum[tid] = w;
     __syncthreads();
     for (int off = kThreads / 2; off > 0; off >>= 1) {
@@ -334,25 +339,6 @@ __global__ __launch_bounds__(256) void fwd_piece_merge_kernel(FwdParams, int n_t
 
 }  // namespace
 
-FwdSplitLayout fwd_split_layout(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
-                                int32_t n_kv_heads, int32_t n_out) {
-  FwdSplitLayout l{};
-  if (n_kv_heads < 1 || n_blocks < 1 || block_size < 1 || n_out < 1) return l;
-  const int64_t n_rows = int64_t(n_blocks) * block_size * (n_q_heads / n_kv_heads);
-  const int64_t n_tiles = (n_rows + kFwdRows - 1) / kFwdRows;
-  const int64_t n_pairs = int64_t(n_kv_heads) * n_out;
-  l.n_codes = n_pairs * n_tiles;
-  l.split_capable = n_pairs < kXcds && l.n_codes <= kSplitMaxItems;
-  if (!l.split_capable) return l;
-  l.grid = l.n_codes + kSplitTargetPieces;
-  // pieces of split items: each has w > P, so ceil(w / P) < 2 w / P, summing below 2 x target
-  l.part_slots = 2 * int64_t(kSplitTargetPieces);
-  l.piece_bytes = sizeof(int32_t) * size_t(l.grid);
-  l.split_bytes = sizeof(int32_t) * size_t(4 + 3 * l.n_codes);
-  l.part_o_bytes = sizeof(float) * size_t(l.part_slots) * kFwdRows * 128;
-  l.part_lse_bytes = sizeof(float) * size_t(l.part_slots) * kFwdRows;
-  return l;
-}
 
 hipError_t launch_fwd_order(const FwdParams& p, int32_t* order, hipStream_t stream) {
   const int G = p.n_q_heads / p.n_kv_heads;
