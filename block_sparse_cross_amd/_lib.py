@@ -51,6 +51,8 @@ _SIGNATURES = [
     ("bsx_abi_version", c_int, []),
     ("bsx_last_error", c_char_p, []),
     ("bsx_status_string", c_char_p, [c_int]),
+    ("bsx_mask_from_anchors", c_int, [POINTER(BsxShape), POINTER(c_int64), POINTER(c_int64),
+                                      POINTER(c_int64), POINTER(c_int64)]),
     ("bsx_validate_mask", c_int, [POINTER(BsxShape), POINTER(c_int64), POINTER(c_int64)]),
     ("bsx_cost_workspace", c_size_t, [c_int32]),
     ("bsx_cost", c_int, [POINTER(BsxShape), c_void_p, c_void_p, POINTER(BsxChunks), c_void_p,
@@ -63,8 +65,8 @@ _SIGNATURES = [
     ("bsx_attn_fwd", c_int, [POINTER(BsxShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_void_p, POINTER(BsxChunks), c_void_p, c_void_p,
                              c_void_p, c_size_t, c_void_p]),
-    ("bsx_lse_merge", c_int, [c_int32, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
-                              c_void_p]),
+    ("bsx_lse_merge", c_int, [c_int32, c_int64, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
+                              c_void_p, c_void_p]),
     ("bsx_bwd_workspace", c_size_t, [POINTER(BsxShape), POINTER(BsxChunks)]),
     ("bsx_attn_bwd", c_int, [POINTER(BsxShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(BsxChunks),

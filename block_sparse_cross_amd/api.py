@@ -111,6 +111,27 @@ def abi_version() -> int:
     return int(lib().bsx_abi_version())
 
 
+def mask_from_anchors(shape: Shape, anchor_global, sample_start=None):
+    """-> (ctx_begin, anchor) int64 host arrays: block b sees [ctx_begin[b], anchor[b])
+    (bsx_mask_from_anchors)."""
+    a = np.ascontiguousarray(anchor_global, dtype=np.int64)
+    if a.shape != (shape.n_blocks,):
+        raise ValueError("anchor_global must have n_blocks entries")
+    s0 = None
+    if sample_start is not None:
+        s0 = np.ascontiguousarray(sample_start, dtype=np.int64)
+        if s0.shape != (shape.n_blocks,):
+            raise ValueError("sample_start must have n_blocks entries")
+    begin = np.empty(shape.n_blocks, np.int64)
+    anchor = np.empty(shape.n_blocks, np.int64)
+    i64 = ctypes.POINTER(ctypes.c_int64)
+    sc = shape.c()
+    check(lib().bsx_mask_from_anchors(ctypes.byref(sc), a.ctypes.data_as(i64),
+                                      None if s0 is None else s0.ctypes.data_as(i64),
+                                      begin.ctypes.data_as(i64), anchor.ctypes.data_as(i64)))
+    return begin, anchor
+
+
 def validate_mask(shape: Shape, anchor, ctx_begin) -> None:
     a = np.ascontiguousarray(anchor, dtype=np.int64)
     b = np.ascontiguousarray(ctx_begin, dtype=np.int64)
@@ -235,9 +256,15 @@ def attn_fwd(shape: Shape, q, k, v, k_self, v_self, anchor, ctx_begin, chunks: C
     return o_part, lse_part
 
 
+_OUT_DTYPES = {torch.float32: BSX_F32, torch.bfloat16: BSX_BF16}
+
+
 def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, o_out=None, lse_out=None,
-              _launch: bool = True):
-    """o_parts [P, *rows, d], lse_parts [P, *rows] (f32) -> (o [*rows, d], lse [*rows])."""
+              out_dtype: torch.dtype = torch.float32, _launch: bool = True):
+    """o_parts [P, *rows, d], lse_parts [P, *rows] (f32) -> (o [*rows, d], lse [*rows]).
+
+    The merged O is f32, or bf16 (rounded to nearest even) with ``out_dtype`` or a bf16
+    ``o_out``."""
     dev = o_parts.device
     P = int(o_parts.shape[0])
     rows_shape = tuple(lse_parts.shape[1:])
@@ -245,16 +272,21 @@ def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, o_out=None, lse_ou
     n_rows = int(np.prod(rows_shape)) if rows_shape else 1
     _need(o_parts, "o_parts", (P, *rows_shape, d), torch.float32, dev)
     _need(lse_parts, "lse_parts", (P, *rows_shape), torch.float32, dev)
+    if o_out is not None:
+        out_dtype = o_out.dtype
+    if out_dtype not in _OUT_DTYPES:
+        raise ValueError(f"merged O dtype {out_dtype} is not float32 or bfloat16")
     if o_out is None:
-        o_out = torch.empty((*rows_shape, d), dtype=torch.float32, device=dev)
+        o_out = torch.empty((*rows_shape, d), dtype=out_dtype, device=dev)
     if lse_out is None:
         lse_out = torch.empty(rows_shape, dtype=torch.float32, device=dev)
-    _need(o_out, "o_out", (*rows_shape, d), torch.float32, dev)
+    _need(o_out, "o_out", (*rows_shape, d), out_dtype, dev)
     _need(lse_out, "lse_out", rows_shape, torch.float32, dev)
     if not _launch:
         return o_out, lse_out
-    check(lib().bsx_lse_merge(P, n_rows, d, _ptr(o_parts), _ptr(lse_parts), _ptr(o_out),
-                              _ptr(lse_out), _stream(o_parts)))
+    check(lib().bsx_lse_merge(P, n_rows, d, _ptr(o_parts), _ptr(lse_parts),
+                              _OUT_DTYPES[out_dtype], _ptr(o_out), _ptr(lse_out),
+                              _stream(o_parts)))
     return o_out, lse_out
 
 
@@ -319,19 +351,22 @@ class Prepared:
     def __init__(self, fn, args: list, keep: list, chunk_slot: Optional[int] = None):
         self._fn = fn
         self._args = args
+        # every tensor and ctypes struct the stored arguments point into, held for the
+        # life of the call (the arguments are raw addresses)
         self._keep = keep
+        self._table = None  # the swapped-in chunk table (host arrays + struct), if any
         self._chunk_slot = chunk_slot
 
     def set_chunks(self, chunks: "Chunks", like: "Chunks") -> None:
         """Swap the chunk table for another with the same slot count and local length
-        (a new plan over the same buffers)."""
+        (a new plan over the same buffers).  The library reads the table during a call
+        only, so the previous swapped-in table is released."""
         if self._chunk_slot is None:
             raise ValueError("this call takes no chunk table")
         if chunks.n_slots != like.n_slots or chunks.n_local != like.n_local:
             raise ValueError("new chunk table does not match the prepared buffers")
         cc = chunks.c()
-        self._keep.append((chunks, cc))
-        del self._keep[:-8]
+        self._table = (chunks, cc)
         self._args[self._chunk_slot] = ctypes.byref(cc)
 
     def __call__(self) -> None:
@@ -378,8 +413,8 @@ def prepare_lse_merge(o_parts, lse_parts, o_out, lse_out) -> Prepared:
     P = int(o_parts.shape[0])
     d = int(o_parts.shape[-1])
     n_rows = int(np.prod(lse_parts.shape[1:])) if lse_parts.dim() > 1 else 1
-    args = [P, n_rows, d, _ptr(o_parts), _ptr(lse_parts), _ptr(o_out), _ptr(lse_out),
-            _stream(o_parts)]
+    args = [P, n_rows, d, _ptr(o_parts), _ptr(lse_parts), _OUT_DTYPES[o_out.dtype], _ptr(o_out),
+            _ptr(lse_out), _stream(o_parts)]
     return _prepare(lib().bsx_lse_merge, args, [o_parts, lse_parts, o_out, lse_out])
 
 
@@ -400,6 +435,6 @@ def prepare_attn_bwd(shape: Shape, q, k, v, k_self, v_self, o, lse, d_o, anchor,
 
 
 __all__ = ["Prepared", "prepare_cost", "prepare_attn_fwd", "prepare_lse_merge",
-           "prepare_attn_bwd", "Shape", "Chunks", "BsxError", "abi_version", "validate_mask", "lpt", "LptResult",
+           "prepare_attn_bwd", "Shape", "Chunks", "BsxError", "abi_version", "mask_from_anchors", "validate_mask", "lpt", "LptResult",
            "cost", "cost_workspace_bytes", "attn_fwd", "fwd_workspace_bytes", "lse_merge",
            "attn_bwd", "bwd_workspace_bytes"]

@@ -225,6 +225,28 @@ bsx_status bsx_validate_mask(const bsx_shape* shape, const int64_t* anchor,
   return ok();
 }
 
+bsx_status bsx_mask_from_anchors(const bsx_shape* shape, const int64_t* anchor_global,
+                                 const int64_t* sample_start, int64_t* ctx_begin,
+                                 int64_t* anchor) {
+  bsx_status st = check_shape(shape, false);
+  if (st != BSX_OK) return st;
+  if (shape->n_blocks > 0 && (!anchor_global || !ctx_begin || !anchor))
+    return fail(BSX_E_INVALID, "anchor_global/ctx_begin/anchor is NULL");
+  // check every block first, so that nothing is written on error
+  for (int32_t b = 0; b < shape->n_blocks; ++b) {
+    const int64_t lo = sample_start ? sample_start[b] : 0, hi = anchor_global[b];
+    if (lo < 0 || lo > hi || hi > shape->ctx_len)
+      return fail(BSX_E_INVALID,
+                  "block %d: anchor %lld with sample start %lld is not inside [0, %lld]", b,
+                  (long long)hi, (long long)lo, (long long)shape->ctx_len);
+  }
+  for (int32_t b = 0; b < shape->n_blocks; ++b) {
+    ctx_begin[b] = sample_start ? sample_start[b] : 0;
+    anchor[b] = anchor_global[b];
+  }
+  return ok();
+}
+
 bsx_status bsx_lpt(int32_t n_items, const int64_t* cost, int32_t n_bins, int32_t* bin_of,
                    int64_t* bin_load, int64_t* makespan, double* imbalance) {
   if (n_items < 0) return fail(BSX_E_INVALID, "n_items = %d < 0", n_items);
@@ -493,18 +515,24 @@ bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, co
 }
 
 bsx_status bsx_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
-                         const float* o_parts, const float* lse_parts, float* o_out,
-                         float* lse_out, void* stream) {
+                         const float* o_parts, const float* lse_parts, int32_t out_dtype,
+                         void* o_out, float* lse_out, void* stream) {
   if (n_parts < 1 || n_parts > 4096)
     return fail(BSX_E_INVALID, "n_parts = %d outside [1, 4096]", n_parts);
   if (n_rows < 0) return fail(BSX_E_INVALID, "n_rows = %lld < 0", (long long)n_rows);
   if (head_dim < 4 || head_dim > 512 || head_dim % 4 != 0)
     return fail(BSX_E_INVALID, "head_dim = %d is not a multiple of 4 in [4, 512]", head_dim);
+  if (out_dtype != BSX_F32 && out_dtype != BSX_BF16)
+    return fail(BSX_E_INVALID, "out_dtype = %d is not BSX_F32 or BSX_BF16", out_dtype);
+  if (out_dtype == BSX_BF16 && n_parts > bsx::kMergeBf16MaxParts)
+    return fail(BSX_E_UNSUPPORTED, "a bf16 merged output takes at most %d partials (got %d)",
+                bsx::kMergeBf16MaxParts, n_parts);
   if (n_rows == 0) return ok();
   if (!o_parts || !lse_parts || !o_out || !lse_out)
     return fail(BSX_E_INVALID, "a merge pointer is NULL");
   return device_status(bsx::launch_lse_merge(n_parts, n_rows, head_dim, o_parts, lse_parts,
-                                             o_out, lse_out, static_cast<hipStream_t>(stream)),
+                                             out_dtype == BSX_BF16, o_out, lse_out,
+                                             static_cast<hipStream_t>(stream)),
                        "merge kernel");
 }
 

@@ -184,9 +184,11 @@ hipError_t launch_fwd_order(const FwdParams& p, int32_t* order, hipStream_t stre
 // Combines the pieces of each split item into o_part / lse_part (split launches).
 hipError_t launch_fwd_piece_merge(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
+// Partials one merge pass weighs at once; a bf16 merged output needs a single pass.
+constexpr int kMergeBf16MaxParts = 128;
 hipError_t launch_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
-                            const float* o_parts, const float* lse_parts, float* o_out,
-                            float* lse_out, hipStream_t stream);
+                            const float* o_parts, const float* lse_parts, bool out_bf16,
+                            void* o_out, float* lse_out, hipStream_t stream);
 // dQ work split: the row tiles (kDqRows query rows of one KV head) are cut into
 // pieces of P key tiles, P chosen so the launch has about kDqTargetWgs workgroups.
 constexpr int kDqRows = 128;

@@ -30,18 +30,35 @@ constexpr int kRowsPerThread = 4;
 constexpr int kRowsPerWg = 32;
 constexpr int kGroups = kThreads / kRowsPerWg;  // lane groups of phase 1
 constexpr int kUnroll = 2;                      // partials in flight per row
-constexpr int kPartsPerPass = 128;              // weights held in LDS at once
+constexpr int kPartsPerPass = kMergeBf16MaxParts;  // weights held in LDS at once
 static_assert(kThreads % kRowsPerWg == 0, "phase 1 needs whole lane groups");
 
 __device__ inline f32x4 load_nt(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
 }
 
+// Stores a merged row piece: f32 as is, or rounded to bf16 (nearest, ties to even).
+template <bool kBf16>
+__device__ inline void store_row(void* o_out, int64_t at, f32x4 v) {
+  if constexpr (kBf16) {
+    typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+    const bf16x4v b = {static_cast<__bf16>(v.x), static_cast<__bf16>(v.y),
+                       static_cast<__bf16>(v.z), static_cast<__bf16>(v.w)};
+    __builtin_nontemporal_store(__builtin_bit_cast(uint64_t, b),
+                                reinterpret_cast<uint64_t*>(static_cast<__bf16*>(o_out) + at));
+  } else {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(o_out) + at));
+  }
+}
+
+// kBf16: the merged O is written as bf16; launched only when one pass of weights covers
+// every partial (the f32 path adds later passes to the rows written so far).
+template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_t n_rows,
                                                              int head_dim,
                                                              const float* __restrict__ o_parts,
                                                              const float* __restrict__ lse_parts,
-                                                             float* __restrict__ o_out,
+                                                             void* __restrict__ o_out,
                                                              float* __restrict__ lse_out) {
   __shared__ float sh_m[kGroups][kRowsPerWg];
   __shared__ float sh_s[kGroups][kRowsPerWg];
@@ -119,7 +136,8 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
         if (!live[k]) r[k] = 0;  // keeps LDS and pointer arithmetic in range
         const int64_t off = (row0 + r[k]) * head_dim + col;
         acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (live[k] && p0 > 0) acc[k] = *reinterpret_cast<const f32x4*>(o_out + off);
+        if (!kBf16 && live[k] && p0 > 0)
+          acc[k] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o_out) + off);
         src[k] = o_parts + int64_t(p0) * pstride + off;
       }
       // loads of partial q for every owned row, or zeros where not needed
@@ -155,9 +173,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
       }
 #pragma unroll
       for (int k = 0; k < kRowsPerThread; ++k)
-        if (live[k])
-          __builtin_nontemporal_store(
-              acc[k], reinterpret_cast<f32x4*>(o_out + (row0 + r[k]) * head_dim + col));
+        if (live[k]) store_row<kBf16>(o_out, (row0 + r[k]) * head_dim + col, acc[k]);
     }
   }
 }
@@ -165,11 +181,17 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
 }  // namespace
 
 hipError_t launch_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
-                            const float* o_parts, const float* lse_parts, float* o_out,
-                            float* lse_out, hipStream_t stream) {
+                            const float* o_parts, const float* lse_parts, bool out_bf16,
+                            void* o_out, float* lse_out, hipStream_t stream) {
   const int64_t blocks = (n_rows + kRowsPerWg - 1) / kRowsPerWg;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, n_parts,
-                     n_rows, head_dim, o_parts, lse_parts, o_out, lse_out);
+  if (out_bf16) {
+    if (n_parts > kPartsPerPass) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(lse_merge_kernel<true>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                       n_parts, n_rows, head_dim, o_parts, lse_parts, o_out, lse_out);
+  } else {
+    hipLaunchKernelGGL(lse_merge_kernel<false>, dim3(unsigned(blocks)), dim3(kThreads), 0,
+                       stream, n_parts, n_rows, head_dim, o_parts, lse_parts, o_out, lse_out);
+  }
   return hipGetLastError();
 }
 

@@ -27,6 +27,10 @@ from . import api
 from .api import Chunks, Shape
 
 
+class MaskError(ValueError):
+    """The cost kernel flagged a block range outside the context."""
+
+
 @dataclass
 class Plan:
     chunk_cost: np.ndarray          # int64 [n_chunks], from the cost kernel
@@ -43,9 +47,12 @@ def make_plan(shape: Shape, chunk_start, chunk_len, mode: str, n_bins: int,
               anchor: torch.Tensor, ctx_begin: torch.Tensor,
               cost_ws: Optional[torch.Tensor] = None, cost_out=None) -> Plan:
     all_chunks = Chunks(chunk_start, chunk_len)
-    _, chunk_cost, _ = api.cost(shape, anchor, ctx_begin, all_chunks, with_counts=False,
-                                ws=cost_ws, out=cost_out)
+    _, chunk_cost, mask_err = api.cost(shape, anchor, ctx_begin, all_chunks, with_counts=False,
+                                       ws=cost_ws, out=cost_out)
     cost_host = chunk_cost.cpu().numpy()
+    if int(mask_err.cpu().item()) != 0:
+        raise MaskError("some draft block's context range [ctx_begin, anchor) is not an "
+                        f"interval of [0, {shape.ctx_len}]: the plan would use clamped ranges")
     start = np.asarray(chunk_start, np.int64)
     length = np.asarray(chunk_len, np.int64)
     n = start.shape[0]

@@ -28,7 +28,7 @@
  *   k, v            [n_local][H_kv][d]   the local chunks back to back, in chunk index order
  *   k_self, v_self  [N_q][H_kv][d]
  *   o_part          [n_out][N_q][H_q][d] f32,  lse_part [n_out][N_q][H_q] f32
- *   merged o        [rows][d] f32,       merged lse [rows] f32  (rows = N_q * H_q)
+ *   merged o        [rows][d] f32 or bf16, merged lse [rows] f32  (rows = N_q * H_q)
  *   anchor, ctx_begin  [n_blocks] int64 (device)
  * LSE values are natural logarithms.  A partial is normalized within its own key set:
  * O_T = sum_{k in T} exp(s_k - LSE_T) v_k.
@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define BSX_ABI_VERSION 1
+#define BSX_ABI_VERSION 2
 
 typedef enum {
   BSX_OK = 0,
@@ -99,6 +99,24 @@ int bsx_abi_version(void);
 /* Text of the last error on this thread ("" when none). */
 const char* bsx_last_error(void);
 const char* bsx_status_string(int status);
+
+/* ---------------------------------------------------------------------------
+ * Host: the block-sparse mask of anchor-sampled draft blocks.  Split-KV page,
+ * Abstract: anchor sampling builds compact draft queries, one draft block per
+ * anchor, which cross-attend the context under a block-sparse mask.  Block b sees
+ * the context positions of its own sample before its anchor:
+ *   ctx_begin[b] = sample_start[b]  (0 when sample_start is NULL: one sample)
+ *   anchor[b]    = anchor_global[b] (packed position of the anchor)
+ * i.e. the interval [ctx_begin[b], anchor[b]) the other calls take, plus (not
+ * stored) the block's own B draft keys.
+ *   anchor_global, sample_start: host [shape->n_blocks]; sample_start may be NULL
+ *   ctx_begin, anchor: host [shape->n_blocks] out, written only on success
+ * Returns BSX_E_INVALID, writing nothing, when some block has
+ * sample_start < 0, sample_start > anchor_global or anchor_global > S.
+ */
+bsx_status bsx_mask_from_anchors(const bsx_shape* shape, const int64_t* anchor_global,
+                                 const int64_t* sample_start, int64_t* ctx_begin,
+                                 int64_t* anchor);
 
 /* ---------------------------------------------------------------------------
  * Host: check a block-sparse mask.  Split-KV page, Abstract (anchor sampling
@@ -164,7 +182,12 @@ bsx_status bsx_place(int32_t mode, int32_t n_items, const int64_t* cost, int32_t
                      int32_t* bin_of, int64_t* bin_load, int64_t* makespan, double* imbalance);
 
 /* ---------------------------------------------------------------------------
- * Device: forward partials.  For every query row (q, h) and output slot s:
+ * Device: forward partials.  Attention is softmax(Q K^T / sqrt(d)) V (Flash-dLLM
+ * page, "Method 1: I/O-Aware Fused KV-Cache Kernel", the attention formula), taken
+ * under the block-sparse draft-query mask over a rank's local KV chunks, each
+ * chunk group giving a partial that the exact merge combines (Split-KV page,
+ * Abstract: exact context parallelism with local key/value shards and a global
+ * query view).  For every query row (q, h) and output slot s:
  * the partial (O, LSE) over the visible keys of the chunks mapped to s; with
  * k_self/v_self given, one more slot (index n_slots, last) over the block's own
  * keys.  n_out = n_slots + (k_self ? 1 : 0).  Rows that see no key of a slot get
@@ -191,17 +214,22 @@ bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, co
  * where partials with LSE_p = -inf are skipped and their O_p is not read; a row
  * whose partials are all -inf merges to (O = 0, LSE = -inf).
  *   o_parts: device [n_parts][n_rows][head_dim] f32; lse_parts: device [n_parts][n_rows] f32
- *   o_out: device [n_rows][head_dim] f32; lse_out: device [n_rows] f32
- * head_dim: a multiple of 4, at most 512.  n_parts: 1 .. 4096.
+ *   out_dtype: BSX_F32 or BSX_BF16, the element type of o_out
+ *   o_out: device [n_rows][head_dim] of out_dtype (BSX_BF16: the f32 result rounded to
+ *          nearest, ties to even); lse_out: device [n_rows] f32
+ * head_dim: a multiple of 4, at most 512.  n_parts: 1 .. 4096 (BSX_F32), 1 .. 128
+ * (BSX_BF16; more returns BSX_E_UNSUPPORTED).
  */
 bsx_status bsx_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
-                         const float* o_parts, const float* lse_parts, float* o_out,
-                         float* lse_out, void* stream);
+                         const float* o_parts, const float* lse_parts, int32_t out_dtype,
+                         void* o_out, float* lse_out, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Device: backward of the attention.  The gradient of the unchunked masked
- * softmax attention with respect to q, k, v, k_self, v_self, using the merged
- * forward results: P = exp(s - LSE), D = rowsum(dO * O), dS = P (dO.v - D),
+ * Device: backward of the attention.  Split-KV page, Abstract: the method trains
+ * diffusion drafters, so the attention (Flash-dLLM page, "Method 1", the
+ * attention formula) needs its gradients; the pages print none, and this is the
+ * analytic gradient of the unchunked masked softmax attention with respect to
+ * q, k, v, k_self, v_self, using the merged forward results: P = exp(s - LSE), D = rowsum(dO * O), dS = P (dO.v - D),
  * dQ = scale dS K, dK = scale dS^T Q (summed over the query heads of a KV head),
  * dV = P^T dO.  Over a chunk subset (one rank's local keys) dK/dV are exact for
  * the local keys and dQ is this share's contribution (shares sum to the full dQ).
