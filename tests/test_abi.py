@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     L = lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.bsx_abi_version() == 1
+    assert L.bsx_abi_version() == 2
 
 
 def test_status_strings():
@@ -85,6 +85,66 @@ def test_validate_mask_matches_oracle():
             bsx.validate_mask(shape, an, be)
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "a3b_s16k", "rank_p64_s1m", "train_pack128k"])
+def test_mask_from_anchors_matches_oracle(name):
+    """Packed anchors and their samples' starts -> each block's context range, bit for bit
+    the oracle's visible_context."""
+    wl = make_workload(get_config(name))
+    c = wl.cfg
+    shape = bsx.Shape(n_blocks=wl.n_blocks, block_size=c.block_size, n_q_heads=c.n_q_heads,
+                      n_kv_heads=c.n_kv_heads, ctx_len=c.ctx_len)
+    sample_start = wl.ctx_begin if c.packed else None
+    begin, anchor = bsx.mask_from_anchors(shape, wl.anchor, sample_start)
+    for b in range(wl.n_blocks):
+        assert (int(begin[b]), int(anchor[b])) == oracle.visible_context(wl.anchor, wl.ctx_begin, b)
+    if c.packed:
+        # each block's range starts at its own sample's first position
+        starts = np.asarray(wl.sample_start)
+        sample_of = np.searchsorted(starts, wl.anchor, side="right") - 1
+        assert np.array_equal(begin, starts[sample_of])
+
+
+def test_mask_from_anchors_rejects_bad_ranges_and_writes_nothing():
+    shape = bsx.Shape(n_blocks=3, block_size=4, n_q_heads=4, n_kv_heads=2, ctx_len=100)
+    i64 = ctypes.POINTER(ctypes.c_int64)
+    for an, st in [([10, 101, 5], [0, 0, 0]), ([10, 50, 5], [0, 60, 0]),
+                   ([10, 50, 5], [-1, 0, 0])]:
+        assert oracle.mask_error(an, st, 100)
+        a = np.asarray(an, np.int64)
+        s0 = np.asarray(st, np.int64)
+        out_b = np.full(3, -7, np.int64)
+        out_a = np.full(3, -7, np.int64)
+        sc = shape.c()
+        assert lib().bsx_mask_from_anchors(ctypes.byref(sc), a.ctypes.data_as(i64),
+                                           s0.ctypes.data_as(i64), out_b.ctypes.data_as(i64),
+                                           out_a.ctypes.data_as(i64)) == BSX_E_INVALID
+        assert np.all(out_b == -7) and np.all(out_a == -7)
+    # without sample starts every range begins at 0
+    begin, anchor = bsx.mask_from_anchors(shape, [0, 100, 37])
+    assert begin.tolist() == [0, 0, 0] and anchor.tolist() == [0, 100, 37]
+
+
+def test_prepared_call_keeps_its_buffers_alive():
+    """A prepared call's arguments are raw addresses: every buffer they point into must stay
+    referenced by the call however many chunk tables are swapped in."""
+    import gc
+    import weakref
+
+    class Buf:
+        pass
+
+    bufs = [Buf() for _ in range(12)]
+    refs = [weakref.ref(b) for b in bufs]
+    call = bsx.Prepared(lambda *a: 0, [0] * 12, list(bufs), chunk_slot=3)
+    del bufs
+    like = bsx.Chunks([0, 10], [10, 10], [0, 1], 2)
+    for i in range(40):
+        call.set_chunks(bsx.Chunks([0, 10], [10, 10], [i % 2, 1 - i % 2], 2), like)
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    call()
+
+
 def _shape(**kw):
     base = dict(n_blocks=2, block_size=16, n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1,
                 ctx_len=1024, scale=0.0)
@@ -133,10 +193,14 @@ def test_forward_rejects_bad_arguments_without_launching():
 
 def test_merge_and_cost_reject_bad_arguments():
     L = lib()
-    assert L.bsx_lse_merge(0, 10, 128, 1, 1, 1, 1, None) == BSX_E_INVALID
-    assert L.bsx_lse_merge(2, 10, 130, 1, 1, 1, 1, None) == BSX_E_INVALID
-    assert L.bsx_lse_merge(2, -1, 128, 1, 1, 1, 1, None) == BSX_E_INVALID
-    assert L.bsx_lse_merge(2, 10, 128, None, 1, 1, 1, None) == BSX_E_INVALID
+    assert L.bsx_lse_merge(0, 10, 128, 1, 1, 0, 1, 1, None) == BSX_E_INVALID
+    assert L.bsx_lse_merge(2, 10, 130, 1, 1, 0, 1, 1, None) == BSX_E_INVALID
+    assert L.bsx_lse_merge(2, -1, 128, 1, 1, 0, 1, 1, None) == BSX_E_INVALID
+    assert L.bsx_lse_merge(2, 10, 128, None, 1, 0, 1, 1, None) == BSX_E_INVALID
+    assert L.bsx_lse_merge(2, 10, 128, 1, 1, 5, 1, 1, None) == BSX_E_INVALID   # out dtype
+    # a bf16 merged output is one weight pass: at most 128 partials
+    assert L.bsx_lse_merge(129, 10, 128, 1, 1, 1, 1, 1, None) == BSX_E_UNSUPPORTED
+    assert b"128" in L.bsx_last_error()
     keep, cc = _chunks([0], [1024])
     sh = _shape()
     assert L.bsx_cost(ctypes.byref(sh), 1, 1, ctypes.byref(cc), 1, 1, None, 1, 1 << 20,

@@ -12,7 +12,8 @@ import torch
 
 import block_sparse_cross_amd as bsx
 import oracle
-from parity_helpers import log, shape_of, upload
+import oracle_pool
+from parity_helpers import log, record, run_bwd, run_fwd, run_merge, shape_of, upload
 from workloads import get_config, make_workload
 from workloads.gen import custom_workload
 
@@ -41,6 +42,8 @@ def _check(name, got, ref, mask=None):
     l2 = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
     log(f"  {name}: max|ref|={scale:.3g} max err={err:.3g} ({err / max(scale, 1e-30):.3g} rel) "
         f"rel-L2={l2:.3g}")
+    record(name, max_ref=float(scale), max_err=float(err), rel=float(err / max(scale, 1e-30)),
+           l2=float(l2))
     if scale == 0:
         assert err == 0, name
         return
@@ -53,11 +56,11 @@ def _gpu_forward_backward(wl, k_loc, v_loc, chunks, with_self=True):
     shape = shape_of(wl)
     ks = dev["k_self"] if with_self else None
     vs = dev["v_self"] if with_self else None
-    o_part, lse_part = bsx.attn_fwd(shape, dev["q"], dev["k"], dev["v"], ks, vs, dev["anchor"],
-                                    dev["ctx_begin"], chunks)
-    o, lse = bsx.lse_merge(o_part, lse_part)
-    grads = bsx.attn_bwd(shape, dev["q"], dev["k"], dev["v"], ks, vs, o, lse, dev["d_o"],
-                         dev["anchor"], dev["ctx_begin"], chunks)
+    o_part, lse_part = run_fwd(shape, dev["q"], dev["k"], dev["v"], ks, vs, dev["anchor"],
+                               dev["ctx_begin"], chunks)
+    o, lse = run_merge(o_part, lse_part)
+    grads = run_bwd(shape, dev["q"], dev["k"], dev["v"], ks, vs, o, lse, dev["d_o"],
+                    dev["anchor"], dev["ctx_begin"], chunks)
     torch.cuda.synchronize()
     return [None if x is None else x.cpu().numpy() for x in grads]
 
@@ -76,6 +79,10 @@ CASES = {
     # 300 chunks (more than the 256-entry LDS copies): chunk list walked from memory
     "many_small_chunks": (4800, 8, 2, 16, [30, 4800, 2400, 1111, 4000], None,
                           list(range(0, 4800, 16)), [16] * 300),
+    # draft blocks larger than a key tile: self keys of several 64-key tiles per block
+    "block80_gqa4": (3000, 8, 2, 80, [0, 1500, 3000, 2999], None, [0, 1000, 2000],
+                     [1000, 1000, 1000]),
+    "block256_gqa2": (2048, 4, 2, 256, [700, 2048, 1], [0, 100, 0], [0, 1024], [1024, 1024]),
     # 64-key tiles spanning distant chunks; rows 64..127 (positions 2024..2087) are seen
     # by no block, so their dK/dV must be exactly zero
     "split_tiles_unseen": (3000, 8, 2, 16, [20, 2010], None, [0, 2000, 900], [40, 100, 30]),
@@ -161,32 +168,24 @@ def test_backward_rank_share_without_self():
     assert pos.shape[0] == dk.shape[0]
 
 
-def test_backward_training_workload_one_kv_head():
+def test_backward_training_workload_all_heads():
     """The full-size training step (8 packed samples, 131072 keys, 16 LPT bins); the oracle
-    computes every gradient of one KV head (all its query heads, keys and draft keys)."""
+    computes every gradient of every KV head (its query heads, keys and draft keys)."""
     wl = make_workload(get_config("train_pack128k"))
     c = wl.cfg
-    log(f"backward, {c.name}: blocks={wl.n_blocks}")
+    log(f"backward, {c.name}: blocks={wl.n_blocks}, all heads")
     k_loc, v_loc = wl.kv_chunks()
     _, cost = oracle.chunk_costs(wl.anchor, wl.ctx_begin, c.block_size, wl.chunk_start,
                                  wl.chunk_len)
     bin_of, *_ = oracle.lpt(cost, c.n_bins)
     chunks = bsx.Chunks(wl.chunk_start, wl.chunk_len, bin_of, c.n_bins)
     dq, dk, dv, dks, dvs = _gpu_forward_backward(wl, k_loc, v_loc, chunks)
-    g = 5
-    o, lse = oracle.attention(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor, wl.ctx_begin,
-                              c.block_size, groups=[g])
-    r = oracle.attention_backward(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
-                                  wl.ctx_begin, c.block_size, wl.chunk_start, wl.chunk_len,
-                                  wl.d_o, np.nan_to_num(o), np.nan_to_num(lse, nan=0.0),
-                                  groups=[g])
-    grp = c.group
-    hs = slice(g * grp, (g + 1) * grp)
-    _check("dq[head group]", dq[:, hs], r[0][:, hs])
-    _check("dk[kv head]", dk[:, g], r[1][:, g])
-    _check("dv[kv head]", dv[:, g], r[2][:, g])
-    _check("dk_self[kv head]", dks[:, g], r[3][:, g])
-    _check("dv_self[kv head]", dvs[:, g], r[4][:, g])
+    r = oracle_pool.backward_all(c.name)
+    _check("dq", dq, r[0])
+    _check("dk", dk, r[1])
+    _check("dv", dv, r[2])
+    _check("dk_self", dks, r[3])
+    _check("dv_self", dvs, r[4])
     # keys past the last sample (the padding tail) are seen by no query
     tail = sum(wl.sample_len)
     assert np.all(dk[tail:] == 0) and np.all(dv[tail:] == 0)
