@@ -9,13 +9,16 @@ exact LSE merge, and for the training workload the backward pass.  Steps are
 pipelined as a training loop runs them: each batch is planned (cost kernel and cost
 readback on a second stream, then the host LPT) while the previous batch's attention
 runs, so every timed step does one whole plan and one whole attention pass.  The
-default workload is the Qwen3.5-35B-A3B-drafter shape (S = 16384, H_q = 32, H_kv = 4,
-d = 128, 32 anchors x 16 draft queries, 16 KV chunks of 1024 with one partial per
-chunk plus the draft block's own keys).
+default workload is the largest one that runs the whole path, forward and backward:
+the packed training step (8 samples packed into 131072 keys, H_q = 32, H_kv = 8,
+d = 128, one anchor per 1024 tokens of a sample with 16 draft queries each, 128 KV
+chunks of 1024 balanced by LPT over 16 bins, plus the draft blocks' own keys).
 
 Prints one JSON line: useful TFLOP/s (masked-out and padded work excluded) of the
-step, a roofline object for the dominant kernel (the forward attention, timed with
-HIP events on the stream it runs on), and the fp64 oracle timed on host cores on a
+step; a roofline object for the dominant call (the backward on the training step,
+else the forward), timed with HIP events on the stream it runs on; forward rooflines
+of the step's workload and of the two other large forward workloads; the standalone
+64-set merge against HBM bandwidth; and the fp64 oracle timed on host cores on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -35,6 +38,7 @@ if ROOT not in sys.path:
 METRIC = "useful TFLOP/s of block-sparse cross-attn fwd (+bwd) and % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak (the f32 path runs plain FMAs)
 
 
 def parse():
@@ -42,7 +46,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="a3b_s16k")
+    ap.add_argument("--workload", default="train_pack128k")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle's CPU baseline sample (0 skips it)")
@@ -56,6 +60,8 @@ def parse():
                     help="print the chunk-placement comparison (imbalance, host us) and exit")
     ap.add_argument("--no-merge-bench", action="store_true",
                     help="skip the standalone 64-set merge measurement")
+    ap.add_argument("--no-extra-fwd", action="store_true",
+                    help="skip the forward rooflines of the other large workloads")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a reference "
                          "dispatch for scaling HBM byte counters)")
@@ -162,7 +168,9 @@ class Step:
                                               self.all_chunks, self.cost_out[1], self.cost_out[2],
                                               ws=self.cost_ws)
         self.cost_host = torch.empty(self.cost_out[1].shape, dtype=torch.int64, pin_memory=True)
+        self.err_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
         self.cost_ready = torch.cuda.Event()
+        self.pending_err = False
         self.next_chunks = None
         self.fwd_call = bsx.prepare_attn_fwd(self.shape, self.q, self.k, self.v, self.ks, self.vs,
                                              self.anchor, self.begin, self.plan0.chunks,
@@ -181,12 +189,21 @@ class Step:
         batch's chunk table (None: the table does not depend on the costs)."""
         c, torch = self.cfg, self.torch
         self.cost_call()
-        if c.slot_mode == "per_chunk":
-            return None  # one partial per chunk: the plan does not depend on the costs
         with torch.cuda.stream(self.side):
-            self.cost_host.copy_(self.cost_out[1], non_blocking=True)
+            if c.slot_mode != "per_chunk":
+                self.cost_host.copy_(self.cost_out[1], non_blocking=True)
+            self.err_host.copy_(self.cost_out[2], non_blocking=True)
             self.cost_ready.record(self.side)
+        if c.slot_mode == "per_chunk":
+            # one partial per chunk: the plan does not depend on the costs; the mask
+            # flag of this batch is checked when the next batch is planned
+            if self.pending_err and int(self.err_host[0]) != 0:
+                raise RuntimeError("cost kernel flagged a block range outside the context")
+            self.pending_err = True
+            return None
         self.cost_ready.synchronize()
+        if int(self.err_host[0]) != 0:
+            raise RuntimeError("cost kernel flagged a block range outside the context")
         r = self.bsx.lpt(self.cost_host.numpy(), c.n_bins)
         wl = self.wl
         if c.slot_mode == "lpt":
@@ -225,21 +242,58 @@ class Step:
         self.next_chunks = (self.plan(),)
 
 
-def time_forward(step: Step, reps: int):
-    """Average duration of one forward launch, from HIP events on the launch stream."""
+def time_call(step: Step, fn, reps: int):
+    """Average duration of one call of ``fn`` (launches on the current stream), from HIP
+    events recorded on that stream around ``reps`` back-to-back calls."""
     torch = step.torch
     stream = torch.cuda.current_stream()
     for _ in range(3):
-        step.forward()
+        fn()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(reps):
-        step.forward()
+        fn()
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / reps * 1e-3
+
+
+def time_forward(step: Step, reps: int):
+    return time_call(step, step.forward, reps)
+
+
+FWD_KERNELS = ["fwd_order_kernel", "fwd_bf16_kernel", "fwd_piece_merge_kernel (split launches)"]
+BWD_KERNELS = ["bwd_delta_kernel", "bwd_dkdv_kernel", "bwd_dq_plan_kernel", "bwd_dq_kernel",
+               "bwd_dq_reduce_kernel"]
+
+
+def fwd_roofline(step: Step, reps: int, workload: str) -> dict:
+    """The forward call (launch-order pass + attention kernel [+ piece merge]): useful
+    forward FLOPs per call over its average duration."""
+    s = time_forward(step, reps)
+    f32 = step.cfg.dtype == "f32"
+    peak = PEAK_F32_TFLOPS if f32 else PEAK_BF16_TFLOPS
+    achieved = step.fwd_flops / s / 1e12
+    return {"bound": "alu" if f32 else "mfma", "achieved": round(achieved, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": None if f32 else recorded_traffic("fwd", workload),
+            "kernel": "fwd_f32_kernel" if f32 else "bsx_attn_fwd: " + " + ".join(FWD_KERNELS),
+            "launch_us": round(s * 1e6, 2), "flops_per_launch": step.fwd_flops}
+
+
+def bwd_roofline(step: Step, reps: int, workload: str) -> dict:
+    """The backward call (all of its kernels): useful backward FLOPs (2.5x the forward's:
+    S recompute, dP, dV, dK, dQ over the visible pairs) over its average duration."""
+    s = time_call(step, step.bwd_call, reps)
+    flops = 2.5 * step.fwd_flops
+    achieved = flops / s / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": recorded_traffic("bwd", workload),
+            "kernel": "bsx_attn_bwd: " + " + ".join(BWD_KERNELS),
+            "launch_us": round(s * 1e6, 2), "flops_per_launch": flops}
 
 
 def merge_bench(device, n_sets: int = 64, rows=(2048, 32), head_dim: int = 128, reps: int = 10,
@@ -276,15 +330,24 @@ def merge_bench(device, n_sets: int = 64, rows=(2048, 32), head_dim: int = 128, 
             "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def _host_cpus():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(wl, plan0, seconds: float):
-    """The fp64 oracle (forward partials of every slot + merge) on (block, KV head) pairs taken
-    in a fixed seeded order until the time budget is spent; useful TFLOP/s of that sample."""
+    """The fp64 oracle as it stands, on (block, KV head) pairs taken in a fixed seeded order
+    until the time budget is spent: forward partials of every slot and their merge, and for
+    training workloads the backward of the same rows (from the oracle's own unchunked
+    forward).  Useful TFLOP/s of that sample (the step's flop count restricted to it)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = 1
+        blas_threads = 1
     c = wl.cfg
     k, v = wl.kv_chunks(plan0.local_chunks)
     ch = plan0.chunks
@@ -293,65 +356,82 @@ def cpu_baseline(wl, plan0, seconds: float):
     pairs = [(b, g) for b in range(wl.n_blocks) for g in range(c.n_kv_heads)]
     order = rng.permutation(len(pairs))
     grp = c.group
+    B = c.block_size
     done_flops, n_done = 0.0, 0
     t0 = time.perf_counter()
     for idx in order:
         b, g = pairs[idx]
         o, lse = oracle.slot_partials(wl.q, k, v, wl.k_self, wl.v_self, wl.anchor, wl.ctx_begin,
-                                      c.block_size, ch.start, ch.length, slot_of, ch.n_slots,
+                                      B, ch.start, ch.length, slot_of, ch.n_slots,
                                       with_self=c.self_slot, blocks=[b], groups=[g])
-        sl = (slice(None), slice(b * c.block_size, (b + 1) * c.block_size),
-              slice(g * grp, (g + 1) * grp))
+        sl = (slice(None), slice(b * B, (b + 1) * B), slice(g * grp, (g + 1) * grp))
         oracle.lse_merge(o[sl].reshape(o.shape[0], -1, o.shape[-1]),
                          lse[sl].reshape(lse.shape[0], -1))
         vis = 0
         for s0, n in zip(ch.start, ch.length):
             vis += max(0, min(int(wl.anchor[b]), s0 + n) - max(int(wl.ctx_begin[b]), s0))
         if c.self_slot:
-            vis += c.block_size
-        done_flops += 4.0 * c.head_dim * grp * c.block_size * vis
+            vis += B
+        flops = 4.0 * c.head_dim * grp * B * vis
+        if c.backward:
+            # the block's rows only: the oracle over a one-block view of the inputs
+            one = slice(b * B, (b + 1) * B)
+            ub, ul = oracle.attention(wl.q[one], k, v, wl.k_self[one], wl.v_self[one],
+                                      wl.anchor[b:b + 1], wl.ctx_begin[b:b + 1], B, groups=[g])
+            oracle.attention_backward(wl.q[one], k, v, wl.k_self[one], wl.v_self[one],
+                                      wl.anchor[b:b + 1], wl.ctx_begin[b:b + 1], B, ch.start,
+                                      ch.length, wl.d_o[one], np.nan_to_num(ub),
+                                      np.nan_to_num(ul, nan=0.0), groups=[g])
+            flops *= 3.5
+        done_flops += flops
         n_done += 1
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+    what = "forward partials of all %d slots + merge%s" % (
+        ch.n_slots + int(c.self_slot), " + backward (dQ, dK, dV)" if c.backward else "")
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s",
+            "cores": int(min(blas_threads, _host_cpus())), "host_cpus": _host_cpus(),
             "kind": "oracle",
-            "sample": f"fp64 oracle forward partials of all {ch.n_slots + int(c.self_slot)} slots "
-                      f"+ merge for {n_done} of {len(pairs)} (block, KV head) pairs of the same "
-                      f"workload, {dt:.1f} s"}
+            "sample": f"fp64 oracle {what} for {n_done} of {len(pairs)} (block, KV head) pairs "
+                      f"of the same workload, {dt:.1f} s; cores = the BLAS threads it ran on"}
 
 
-# Sources of the forward kernel; the recorded HBM traffic is valid only for them (of the
-# shared internal header, only the declarations the forward kernel reads).
-FWD_SOURCES = ["block_sparse_cross_amd/csrc/fwd_bf16.hip", "block_sparse_cross_amd/csrc/fwd_common.h",
-               "block_sparse_cross_amd/csrc/mfma_common.h"]
-FWD_HEADER = "block_sparse_cross_amd/csrc/bsx_internal.h"
+# Sources of each call's kernels; a recorded HBM traffic figure is valid only while they
+# are unchanged (of the shared internal header, only the declarations the kernels read).
+CALL_SOURCES = {
+    "fwd": ["block_sparse_cross_amd/csrc/fwd_bf16.hip", "block_sparse_cross_amd/csrc/fwd_order.hip",
+            "block_sparse_cross_amd/csrc/fwd_common.h", "block_sparse_cross_amd/csrc/mfma_common.h"],
+    "bwd": ["block_sparse_cross_amd/csrc/bwd_bf16.hip", "block_sparse_cross_amd/csrc/fwd_common.h",
+            "block_sparse_cross_amd/csrc/mfma_common.h"],
+}
+INTERNAL_HEADER = "block_sparse_cross_amd/csrc/bsx_internal.h"
 
 
-def fwd_sources_sha256() -> str:
+def sources_sha256(call: str) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in FWD_SOURCES:
+    for rel in CALL_SOURCES[call]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
-    with open(os.path.join(ROOT, FWD_HEADER), "rb") as f:
-        text = f.read()
-    h.update(text[text.index(b"struct ChunkEntry"):text.index(b"struct BwdParams")])
+    with open(os.path.join(ROOT, INTERNAL_HEADER), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per forward launch from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by the elementwise-kernel calibration), or None when
-    there is none for this workload or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"fwd_bf16_{workload}_counters.md")
+def recorded_traffic(call: str, workload: str):
+    """HBM bytes per call from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE of the call's kernels, scaled by the elementwise-kernel
+    calibration), or None when there is none for this workload or the kernel sources
+    changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{call}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         for line in f:
             if line.startswith("traffic_record: "):
                 rec = json.loads(line[len("traffic_record: "):])
-                if rec.get("sources_sha256") == fwd_sources_sha256():
+                if rec.get("sources_sha256") == sources_sha256(call):
                     return rec["bytes_per_launch"]
     return None
 
@@ -428,14 +508,29 @@ def cost_stress(device, reps: int = 20):
             "mask_err": int(err.item())}
 
 
-def planner_comparison(device, reps: int = 200):
+def planner_comparison(device, reps: int = 2000):
     """Chunk placements on the planned workloads' realized costs (cost kernel on the GPU):
-    imbalance and host time per plan for LPT and the static layouts the pages compare."""
+    imbalance and host time per plan for LPT and the static layouts the pages compare.
+    Host time is the C call alone: the library entry point is called through ctypes with
+    its arguments marshalled once, and the same loop around a call that returns at once
+    (bsx_abi_version) is subtracted."""
+    import ctypes
+
     import torch
 
     import block_sparse_cross_amd as bsx
+    from block_sparse_cross_amd._lib import lib
     from workloads import get_config, make_workload
 
+    L = lib()
+
+    def loop_ns(fn, args):
+        t0 = time.perf_counter_ns()
+        for _ in range(reps):
+            fn(*args)
+        return (time.perf_counter_ns() - t0) / reps
+
+    base = min(loop_ns(L.bsx_abi_version, ()) for _ in range(5))
     out = {}
     for name in ("b27_s64k", "rank_p64_s1m", "train_pack128k"):
         cfg = get_config(name)
@@ -445,18 +540,23 @@ def planner_comparison(device, reps: int = 200):
         be = torch.from_numpy(wl.ctx_begin).to(device)
         _, cost, _ = bsx.cost(shape, an, be, bsx.Chunks(wl.chunk_start, wl.chunk_len),
                               with_counts=False)
-        cost = cost.cpu().numpy()
-        res = {"n_chunks": int(cost.shape[0]), "n_bins": cfg.n_bins}
+        cost = np.ascontiguousarray(cost.cpu().numpy(), np.int64)
+        n, P = int(cost.shape[0]), int(cfg.n_bins)
+        bin_of = np.empty(n, np.int32)
+        loads = np.empty(P, np.int64)
+        ms, imb = ctypes.c_int64(0), ctypes.c_double(0.0)
+        res = {"n_chunks": n, "n_bins": P}
         for mode in ("lpt", "zigzag", "round_robin", "contiguous"):
-            r = bsx.place(mode, cost, cfg.n_bins)
-            ts = []
-            for _ in range(reps):
-                t0 = time.perf_counter_ns()
-                bsx.place(mode, cost, cfg.n_bins)
-                ts.append(time.perf_counter_ns() - t0)
-            res[mode] = {"imbalance": round(r.imbalance, 5),
-                         "host_us": round(float(np.median(ts)) / 1e3, 2)}
+            r = bsx.place(mode, cost, P)
+            args = (bsx.api.PLACEMENTS[mode], n, cost.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                    P, bin_of.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                    loads.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ctypes.byref(ms),
+                    ctypes.byref(imb))
+            ns = min(loop_ns(L.bsx_place, args) for _ in range(5))
+            res[mode] = {"imbalance": round(r.imbalance, 5), "ns_per_call": round(ns, 1),
+                         "ns_net_of_call_overhead": round(ns - base, 1)}
         out[name] = res
+    out["call_overhead_ns"] = round(base, 1)
     return out
 
 
@@ -483,7 +583,8 @@ def main():
         return
     if args.planners:
         print(json.dumps({"planners": planner_comparison(dev),
-                          "note": "host_us: median per call through the Python binding"}),
+                          "note": "ns_per_call: the C entry point through ctypes with "
+                                  "pre-marshalled arguments; net: minus an empty call"}),
               flush=True)
         return
     if args.calibrate_copy_mib > 0:
@@ -516,13 +617,28 @@ def main():
     ms = dt / args.steps * 1e3
     value = step.step_flops / (dt / args.steps) / 1e12
 
-    fwd_s = time_forward(step, args.fwd_reps)
-    achieved = step.fwd_flops / fwd_s / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": recorded_traffic(cfg.name), "kernel": "fwd_bf16_kernel",
-                "launch_us": round(fwd_s * 1e6, 2),
-                "flops_per_launch": step.fwd_flops}
+    # the dominant call of the step (the backward on the training workload) gives the
+    # roofline; the forward call's roofline is reported beside it
+    fwd_rl = fwd_roofline(step, args.fwd_reps, cfg.name)
+    roofline = fwd_rl
+    bwd_rl = None
+    if step.bwd_call is not None:
+        bwd_rl = bwd_roofline(step, args.fwd_reps, cfg.name)
+        if bwd_rl["launch_us"] > fwd_rl["launch_us"]:
+            roofline = bwd_rl
+    other_fwd = {}
+    if not args.no_extra_fwd and cfg.dtype == "bf16":
+        # the forward of the other two large workloads, in the launch configuration their
+        # steps use (LPT-bin slots; one rank's fused share)
+        for name in ("b27_s64k", "rank_p64_s1m"):
+            if name == cfg.name:
+                continue
+            wl2 = make_workload(get_config(name))
+            st2 = Step(wl2, dev)
+            st2.prepare()
+            other_fwd[name] = fwd_roofline(st2, args.fwd_reps, name)
+            del st2
+            torch.cuda.empty_cache()
     merge = None if args.no_merge_bench else merge_bench(dev)
     cpu = None
     if args.cpu_seconds > 0:
@@ -542,6 +658,9 @@ def main():
                    "n_chunks": wl.n_chunks, "slot_mode": c.slot_mode, "n_bins": c.n_bins,
                    "backward": c.backward, "seed": wl.cfg.seed},
         "roofline": roofline,
+        "fwd_roofline": fwd_rl,
+        "bwd_roofline": bwd_rl,
+        "fwd_roofline_other_workloads": other_fwd or None,
         "merge_roofline": merge,
         "cpu_baseline": cpu,
     }
