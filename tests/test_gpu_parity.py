@@ -494,8 +494,9 @@ def test_merge_rank_sets_full_size_all_rows():
 @pytest.mark.parametrize("P,R", [(17, 512 * 32), (64, 1000), (128, 77)])
 def test_merge_bf16_output(P, R):
     """The bf16 merged output is the f32 merged output rounded to nearest even: bit-exact
-    against the library's own f32 result rounded, and within one bf16 ulp of the oracle's
-    fp64 result rounded."""
+    against the library's own f32 result rounded, and within one bf16 ulp (plus the f32
+    path's own 1e-5 tolerance, which decides the rounding of values near zero) of the
+    oracle's fp64 result rounded."""
     from workloads.gen import round_to_bf16
     rng = np.random.default_rng(P * 7 + R)
     o = rng.standard_normal((P, R, 128)).astype(np.float32)
@@ -513,7 +514,7 @@ def test_merge_bf16_output(P, R):
     want = round_to_bf16(ro.astype(np.float32))
     # one bf16 ulp of the rounded value (2^-7 relative to its binade)
     ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(want), 1e-30))[1] - 8)
-    assert np.all(np.abs(got - want) <= ulp)
+    assert np.all(np.abs(got - want) <= ulp + 1e-5)
     assert np.all(got[5] == 0) and np.isneginf(ml16.cpu().numpy()[5])
 
 
