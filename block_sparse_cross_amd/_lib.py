@@ -65,6 +65,9 @@ _SIGNATURES = [
     ("bsx_attn_fwd", c_int, [POINTER(BsxShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_void_p, POINTER(BsxChunks), c_void_p, c_void_p,
                              c_void_p, c_size_t, c_void_p]),
+    ("bsx_attn_fwd_noalloc", c_int, [POINTER(BsxShape), c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, POINTER(BsxChunks), c_void_p,
+                                     c_void_p, c_void_p]),
     ("bsx_lse_merge", c_int, [c_int32, c_int64, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
                               c_void_p, c_void_p]),
     ("bsx_bwd_workspace", c_size_t, [POINTER(BsxShape), POINTER(BsxChunks)]),

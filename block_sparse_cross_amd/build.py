@@ -29,6 +29,7 @@ SOURCES = [
     "fwd_bf16.hip",
     "fwd_order.hip",
     "bwd_bf16.hip",
+    "noalloc.hip",
 ]
 
 ARCH = "gfx950"

@@ -19,20 +19,20 @@
 
 namespace {
 
-thread_local std::string g_last_error;
+// Text of the last error on this thread (a fixed buffer: reporting an error allocates
+// nothing).
+thread_local char g_last_error[512];
 
 bsx_status fail(bsx_status st, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return st;
 }
 
 bsx_status ok() {
-  g_last_error.clear();
+  g_last_error[0] = '\0';
   return BSX_OK;
 }
 
@@ -129,60 +129,96 @@ FwdLayout fwd_layout(int32_t n_slots, int32_t n_chunks) {
 
 // Places a host-built table inline in the kernel arguments when it fits, else
 // uploads it to the workspace on `stream` and points the kernels there.
-hipError_t place_table(const std::vector<uint32_t>& words, void* ws, hipStream_t stream,
+hipError_t place_table(const uint32_t* words, size_t n_words, void* ws, hipStream_t stream,
                        bsx::ChunkTable* t) {
   std::memset(t, 0, sizeof(*t));
-  if (words.size() * 4 <= size_t(bsx::kInlineBytes)) {
-    if (!words.empty()) std::memcpy(t->words, words.data(), words.size() * 4);
+  if (n_words * 4 <= size_t(bsx::kInlineBytes)) {
+    if (n_words) std::memcpy(t->words, words, n_words * 4);
     t->dev = nullptr;
     return hipSuccess;
   }
   t->dev = static_cast<const char*>(ws);
-  return bsx::launch_upload(words.data(), words.size(), static_cast<uint32_t*>(ws), stream);
+  return bsx::launch_upload(words, n_words, static_cast<uint32_t*>(ws), stream);
+}
+
+hipError_t place_table(const std::vector<uint32_t>& words, void* ws, hipStream_t stream,
+                       bsx::ChunkTable* t) {
+  return place_table(words.data(), words.size(), ws, stream, t);
+}
+
+// Storage the forward descriptor is built in, provided by the caller (the builder
+// itself allocates nothing).
+struct FwdDescStorage {
+  int64_t* off;            // [n_chunks]
+  int32_t* ptr;            // [n_slots + 1]
+  int32_t* fill;           // [n_slots]
+  bsx::ChunkEntry* ent;    // [n_chunks]
+  bsx::ChunkEntry* tmp;    // [n_chunks]
+  uint32_t* words;         // [fwd_desc_words(n_slots, n_chunks)]
+};
+
+size_t fwd_desc_words(int32_t n_slots, int32_t n_chunks) {
+  return align_up(fwd_layout(n_slots, n_chunks).total, 4) / 4;
+}
+
+// Stable sort of a[0, n) by start (bottom-up merge sort through tmp).
+void sort_by_start(bsx::ChunkEntry* a, int32_t n, bsx::ChunkEntry* tmp) {
+  bsx::ChunkEntry* src = a;
+  bsx::ChunkEntry* dst = tmp;
+  for (int32_t width = 1; width < n; width *= 2) {
+    for (int32_t lo = 0; lo < n; lo += 2 * width) {
+      const int32_t mid = std::min(lo + width, n), hi = std::min(lo + 2 * width, n);
+      int32_t i = lo, j = mid, k = lo;
+      while (i < mid && j < hi) dst[k++] = src[j].start < src[i].start ? src[j++] : src[i++];
+      while (i < mid) dst[k++] = src[i++];
+      while (j < hi) dst[k++] = src[j++];
+    }
+    std::swap(src, dst);
+  }
+  if (src != a) std::memcpy(a, src, sizeof(bsx::ChunkEntry) * size_t(n));
 }
 
 // Each slot's entries are sorted by start (ties keep chunk index order); *order is 2
 // when every slot's entries are also disjoint, else 1.  Kernels walking a slot stop at
 // its first entry past their range, and bisect to their first entry when disjoint.
-void build_fwd_descriptor(const bsx_chunks* c, std::vector<uint32_t>* words, int32_t* n_entries,
-                          int32_t* order) {
+// Returns the descriptor's length in 32-bit words (in st.words).
+size_t build_fwd_descriptor(const bsx_chunks* c, const FwdDescStorage& st, int32_t* n_entries,
+                            int32_t* order) {
   const int32_t nc = c->n_chunks, ns = c->n_slots;
   const FwdLayout l = fwd_layout(ns, nc);
-  std::vector<int64_t> off(nc);
   int64_t acc = 0;
   for (int32_t i = 0; i < nc; ++i) {
-    off[i] = acc;
+    st.off[i] = acc;
     acc += c->len[i];
   }
-  std::vector<int32_t> count(ns + 1, 0);
+  for (int32_t s = 0; s <= ns; ++s) st.ptr[s] = 0;
   for (int32_t i = 0; i < nc; ++i)
-    if (c->len[i] > 0) count[(c->slot ? c->slot[i] : i) + 1]++;
-  std::vector<int32_t> ptr(ns + 1, 0);
-  for (int32_t s = 0; s < ns; ++s) ptr[s + 1] = ptr[s] + count[s + 1];
-  std::vector<bsx::ChunkEntry> ent(ptr[ns]);
-  std::vector<int32_t> fill(ptr.begin(), ptr.end() - 1);
+    if (c->len[i] > 0) st.ptr[(c->slot ? c->slot[i] : i) + 1]++;
+  for (int32_t s = 0; s < ns; ++s) st.ptr[s + 1] += st.ptr[s];
+  for (int32_t s = 0; s < ns; ++s) st.fill[s] = st.ptr[s];
   for (int32_t i = 0; i < nc; ++i) {
     if (c->len[i] <= 0) continue;
     const int32_t s = c->slot ? c->slot[i] : i;
-    ent[fill[s]++] = bsx::ChunkEntry{c->start[i], uint32_t(c->len[i]), uint32_t(off[i])};
+    st.ent[st.fill[s]++] = bsx::ChunkEntry{c->start[i], uint32_t(c->len[i]), uint32_t(st.off[i])};
   }
   bool disjoint = true;
   for (int32_t s = 0; s < ns; ++s) {
-    const auto b = ent.begin() + ptr[s], z = ent.begin() + ptr[s + 1];
-    std::stable_sort(b, z, [](const bsx::ChunkEntry& x, const bsx::ChunkEntry& y) {
-      return x.start < y.start;
-    });
-    for (auto it = b; it + 1 < z; ++it)
-      if (it->start + int64_t(it->len) > (it + 1)->start) disjoint = false;
+    bsx::ChunkEntry* b = st.ent + st.ptr[s];
+    const int32_t n = st.ptr[s + 1] - st.ptr[s];
+    sort_by_start(b, n, st.tmp);
+    for (int32_t j = 0; j + 1 < n; ++j)
+      if (b[j].start + int64_t(b[j].len) > b[j + 1].start) disjoint = false;
   }
   *order = disjoint ? 2 : 1;
-  const size_t used = l.entries_off + sizeof(bsx::ChunkEntry) * ent.size();
-  words->assign(align_up(used, 4) / 4, 0u);
-  std::memcpy(words->data(), ptr.data(), l.ptr_bytes);
-  if (!ent.empty())
-    std::memcpy(reinterpret_cast<char*>(words->data()) + l.entries_off, ent.data(),
-                sizeof(bsx::ChunkEntry) * ent.size());
-  *n_entries = ptr[ns];
+  const size_t used = l.entries_off + sizeof(bsx::ChunkEntry) * size_t(st.ptr[ns]);
+  const size_t n_words = align_up(used, 4) / 4;
+  std::memset(st.words, 0, n_words * 4);
+  std::memcpy(st.words, st.ptr, l.ptr_bytes);
+  if (st.ptr[ns] > 0)
+    std::memcpy(reinterpret_cast<char*>(st.words) + l.entries_off, st.ent,
+                sizeof(bsx::ChunkEntry) * size_t(st.ptr[ns]));
+  *n_entries = st.ptr[ns];
+  return n_words;
 }
 
 float resolve_scale(const bsx_shape* s) {
@@ -197,7 +233,7 @@ extern "C" {
 
 int bsx_abi_version(void) { return BSX_ABI_VERSION; }
 
-const char* bsx_last_error(void) { return g_last_error.c_str(); }
+const char* bsx_last_error(void) { return g_last_error; }
 
 const char* bsx_status_string(int status) {
   switch (status) {
@@ -390,7 +426,10 @@ struct FwdWs {
   size_t total = 0;
 };
 
-FwdWs fwd_ws_layout(const bsx_shape* shape, const bsx_chunks* chunks, int64_t n_out) {
+// allow_split: launches with few (KV head, slot) pairs may cut long items into pieces,
+// which needs room for the pieces' partials; without it such launches run unsplit.
+FwdWs fwd_ws_layout(const bsx_shape* shape, const bsx_chunks* chunks, int64_t n_out,
+                    bool allow_split = true) {
   FwdWs w;
   w.total = align_up(fwd_layout(chunks->n_slots, chunks->n_chunks).total, 256);
   if (!shape || shape->dtype != BSX_BF16 || shape->n_kv_heads < 1 || shape->n_blocks < 1 ||
@@ -402,15 +441,15 @@ FwdWs fwd_ws_layout(const bsx_shape* shape, const bsx_chunks* chunks, int64_t n_
   if (n_tiles * n_out > bsx::kOrderMaxItems) return w;
   const bsx::FwdSplitLayout sl = bsx::fwd_split_layout(
       shape->n_blocks, shape->block_size, shape->n_q_heads, shape->n_kv_heads, int32_t(n_out));
-  const int64_t grid = sl.split_capable
-                           ? sl.grid
-                           : bsx::fwd_bf16_grid(shape->n_blocks, shape->block_size,
-                                                shape->n_q_heads, shape->n_kv_heads,
-                                                int32_t(n_out));
+  const bool split = allow_split && sl.split_capable;
+  const int64_t grid = split ? sl.grid
+                             : bsx::fwd_bf16_grid(shape->n_blocks, shape->block_size,
+                                                  shape->n_q_heads, shape->n_kv_heads,
+                                                  int32_t(n_out));
   w.order = true;
   w.order_off = w.total;
   w.total += align_up(sizeof(int32_t) * size_t(grid), 256);
-  if (sl.split_capable) {
+  if (split) {
     w.split = true;
     w.piece_off = w.total;
     w.total += align_up(sl.piece_bytes, 256);
@@ -424,42 +463,43 @@ FwdWs fwd_ws_layout(const bsx_shape* shape, const bsx_chunks* chunks, int64_t n_
   return w;
 }
 
-size_t bsx_fwd_workspace(const bsx_shape* shape, const bsx_chunks* chunks) {
-  if (!chunks || chunks->n_chunks < 0 || chunks->n_slots < 0) return 0;
-  const size_t with_self = fwd_ws_layout(shape, chunks, int64_t(chunks->n_slots) + 1).total;
-  const size_t without = fwd_ws_layout(shape, chunks, chunks->n_slots).total;
-  return with_self > without ? with_self : without;
-}
-
-bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, const void* v,
-                        const void* k_self, const void* v_self, const int64_t* anchor,
-                        const int64_t* ctx_begin, const bsx_chunks* chunks, float* o_part,
-                        float* lse_part, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks of a forward call (all but the workspace).  *n_local is the local
+// K/V length; *empty is true when there is nothing to compute.
+bsx_status check_fwd_args(const bsx_shape* shape, const void* q, const void* k, const void* v,
+                          const void* k_self, const void* v_self, const int64_t* anchor,
+                          const int64_t* ctx_begin, const bsx_chunks* chunks,
+                          const float* o_part, const float* lse_part, int64_t* n_local,
+                          bool* empty) {
   bsx_status st = check_shape(shape, true);
   if (st != BSX_OK) return st;
-  int64_t n_local = 0;
-  st = check_chunks(shape, chunks, true, &n_local);
+  st = check_chunks(shape, chunks, true, n_local);
   if (st != BSX_OK) return st;
   if ((k_self == nullptr) != (v_self == nullptr))
     return fail(BSX_E_INVALID, "k_self and v_self must both be given or both be NULL");
-  const int has_self = k_self != nullptr;
-  const int64_t n_out = int64_t(chunks->n_slots) + has_self;
-  if (shape->n_blocks == 0 || n_out == 0) return ok();
+  const int64_t n_out = int64_t(chunks->n_slots) + (k_self != nullptr);
+  *empty = shape->n_blocks == 0 || n_out == 0;
+  if (*empty) return ok();
   if (!q || !anchor || !ctx_begin || !o_part || !lse_part)
     return fail(BSX_E_INVALID, "q/anchor/ctx_begin/o_part/lse_part is NULL");
-  if (n_local > 0 && (!k || !v)) return fail(BSX_E_INVALID, "k/v is NULL");
-  const size_t need = bsx_fwd_workspace(shape, chunks);
-  if (!ws || ws_bytes < need)
-    return fail(BSX_E_WORKSPACE, "workspace of %zu bytes is smaller than %zu", ws_bytes, need);
+  if (*n_local > 0 && (!k || !v)) return fail(BSX_E_INVALID, "k/v is NULL");
+  return ok();
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  std::vector<uint32_t> words;
+// Builds the forward descriptor in `st` and launches the forward pass; `ws` holds the
+// pieces of layout `w` (the table when it is not inline, the launch order, the split
+// tables).
+bsx_status launch_forward(const bsx_shape* shape, const void* q, const void* k, const void* v,
+                          const void* k_self, const void* v_self, const int64_t* anchor,
+                          const int64_t* ctx_begin, const bsx_chunks* chunks, int64_t n_local,
+                          float* o_part, float* lse_part, const FwdDescStorage& st,
+                          const FwdWs& w, void* ws, hipStream_t s) {
   int32_t n_entries = 0, entries_order = 0;
-  build_fwd_descriptor(chunks, &words, &n_entries, &entries_order);
+  const size_t n_words = build_fwd_descriptor(chunks, st, &n_entries, &entries_order);
   const FwdLayout l = fwd_layout(chunks->n_slots, chunks->n_chunks);
+  const int has_self = k_self != nullptr;
 
   bsx::FwdParams p{};
-  hipError_t e = place_table(words, ws, s, &p.table);
+  hipError_t e = place_table(st.words, n_words, ws, s, &p.table);
   if (e != hipSuccess) return device_status(e, "forward descriptor upload");
   p.entries_off = uint32_t(l.entries_off);
   p.entries_order = entries_order;
@@ -492,7 +532,6 @@ bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, co
     // costs one small launch and pays for itself even when items are at most one chunk
     // long (measured on 16 one-chunk LPT bins).  Launches with few items may also split
     // long items into pieces (merged afterwards).
-    const FwdWs w = fwd_ws_layout(shape, chunks, n_out);
     char* base = static_cast<char*>(ws);
     if (w.order) {
       int32_t* order = reinterpret_cast<int32_t*>(base + w.order_off);
@@ -512,6 +551,75 @@ bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, co
     e = bsx::launch_fwd_f32(p, s);
   }
   return device_status(e, "forward kernel");
+}
+
+size_t bsx_fwd_workspace(const bsx_shape* shape, const bsx_chunks* chunks) {
+  if (!chunks || chunks->n_chunks < 0 || chunks->n_slots < 0) return 0;
+  const size_t with_self = fwd_ws_layout(shape, chunks, int64_t(chunks->n_slots) + 1).total;
+  const size_t without = fwd_ws_layout(shape, chunks, chunks->n_slots).total;
+  return with_self > without ? with_self : without;
+}
+
+bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, const void* v,
+                        const void* k_self, const void* v_self, const int64_t* anchor,
+                        const int64_t* ctx_begin, const bsx_chunks* chunks, float* o_part,
+                        float* lse_part, void* ws, size_t ws_bytes, void* stream) {
+  int64_t n_local = 0;
+  bool empty = false;
+  bsx_status st = check_fwd_args(shape, q, k, v, k_self, v_self, anchor, ctx_begin, chunks,
+                                 o_part, lse_part, &n_local, &empty);
+  if (st != BSX_OK || empty) return st;
+  const size_t need = bsx_fwd_workspace(shape, chunks);
+  if (!ws || ws_bytes < need)
+    return fail(BSX_E_WORKSPACE, "workspace of %zu bytes is smaller than %zu", ws_bytes, need);
+  const int32_t nc = chunks->n_chunks, ns = chunks->n_slots;
+  std::vector<int64_t> off(size_t(nc) + 1);
+  std::vector<int32_t> ptr(size_t(ns) + 1), fill(size_t(ns) + 1);
+  std::vector<bsx::ChunkEntry> ent(size_t(nc) + 1), tmp(size_t(nc) + 1);
+  std::vector<uint32_t> words(fwd_desc_words(ns, nc) + 1);
+  const FwdDescStorage storage{off.data(), ptr.data(), fill.data(), ent.data(), tmp.data(),
+                               words.data()};
+  const int64_t n_out = int64_t(ns) + (k_self != nullptr);
+  return launch_forward(shape, q, k, v, k_self, v_self, anchor, ctx_begin, chunks, n_local,
+                        o_part, lse_part, storage, fwd_ws_layout(shape, chunks, n_out), ws,
+                        static_cast<hipStream_t>(stream));
+}
+
+bsx_status bsx_attn_fwd_noalloc(const bsx_shape* shape, const void* q, const void* k,
+                                const void* v, const void* k_self, const void* v_self,
+                                const int64_t* anchor, const int64_t* ctx_begin,
+                                const bsx_chunks* chunks, float* o_part, float* lse_part,
+                                void* stream) {
+  int64_t n_local = 0;
+  bool empty = false;
+  bsx_status st = check_fwd_args(shape, q, k, v, k_self, v_self, anchor, ctx_begin, chunks,
+                                 o_part, lse_part, &n_local, &empty);
+  if (st != BSX_OK || empty) return st;
+  constexpr int32_t kMax = BSX_NOALLOC_MAX_CHUNKS;
+  if (chunks->n_chunks > kMax || chunks->n_slots > kMax)
+    return fail(BSX_E_UNSUPPORTED,
+                "bsx_attn_fwd_noalloc takes at most %d chunks and %d slots (got %d, %d)", kMax,
+                kMax, chunks->n_chunks, chunks->n_slots);
+  const int64_t n_out = int64_t(chunks->n_slots) + (k_self != nullptr);
+  const FwdWs w = fwd_ws_layout(shape, chunks, n_out, /*allow_split=*/false);
+  if (w.total > size_t(BSX_NOALLOC_SCRATCH_BYTES))
+    return fail(BSX_E_UNSUPPORTED,
+                "this forward needs %zu bytes of scratch; bsx_attn_fwd_noalloc has %zu",
+                w.total, size_t(BSX_NOALLOC_SCRATCH_BYTES));
+  // descriptor storage on the stack, sized for the largest table this entry point takes
+  int64_t off[kMax];
+  int32_t ptr[kMax + 1], fill[kMax + 1];
+  bsx::ChunkEntry ent[kMax], tmp[kMax];
+  uint32_t words[(16 * (kMax + 1) + 16 * kMax) / 4 + 4];
+  static_assert(sizeof(words) / 4 >= (sizeof(int32_t) * (kMax + 1) + 15) / 16 * 4 + 4 * kMax,
+                "descriptor words of the largest table fit");
+  const FwdDescStorage storage{off, ptr, fill, ent, tmp, words};
+  hipError_t e = hipSuccess;
+  void* scratch = bsx::noalloc_scratch(&e);
+  if (!scratch) return device_status(e == hipSuccess ? hipErrorInvalidDevice : e,
+                                     "scratch address of the current device");
+  return launch_forward(shape, q, k, v, k_self, v_self, anchor, ctx_begin, chunks, n_local,
+                        o_part, lse_part, storage, w, scratch, static_cast<hipStream_t>(stream));
 }
 
 bsx_status bsx_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,

@@ -206,4 +206,9 @@ DqLayout bwd_dq_layout(int32_t n_blocks, int32_t block_size, int32_t n_q_heads,
                        int32_t n_kv_heads);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 
+// The current device's copy of the no-allocation scratch array (BSX_NOALLOC_SCRATCH_BYTES,
+// 256-byte aligned), its address looked up once per device; null with *err set when the
+// device or the lookup fails.
+void* noalloc_scratch(hipError_t* err);
+
 }  // namespace bsx

@@ -208,6 +208,29 @@ bsx_status bsx_attn_fwd(const bsx_shape* shape, const void* q, const void* k, co
                         float* lse_part, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Device: bsx_attn_fwd without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and errors as bsx_attn_fwd, minus ws/ws_bytes:
+ * its scratch (the uploaded chunk table and the launch order) lives in a file-scope
+ * device array of BSX_NOALLOC_SCRATCH_BYTES that each GPU holds from the library's
+ * load until the process ends.  The call allocates nothing: no hipMalloc/hipFree and
+ * no host heap.  Limits (BSX_E_UNSUPPORTED beyond them, nothing launched): at most
+ * BSX_NOALLOC_MAX_CHUNKS chunks and slots, and a launch whose table and launch order
+ * fit the scratch.  Launches with few (KV head, slot) pairs run without the split of
+ * long items that bsx_attn_fwd may use (same results within rounding).  Every call
+ * on a GPU shares that GPU's scratch, which keeps the last call's contents: calls
+ * that overlap on one GPU (on different streams or threads) race and must be
+ * serialized by the caller.
+ */
+#define BSX_NOALLOC_MAX_CHUNKS 1024
+#define BSX_NOALLOC_SCRATCH_BYTES (1 << 20)
+bsx_status bsx_attn_fwd_noalloc(const bsx_shape* shape, const void* q, const void* k,
+                                const void* v, const void* k_self, const void* v_self,
+                                const int64_t* anchor, const int64_t* ctx_begin,
+                                const bsx_chunks* chunks, float* o_part, float* lse_part,
+                                void* stream);
+
+/* ---------------------------------------------------------------------------
  * Device: exact LSE merge of partials.  Split-KV page, Abstract (exact method,
  * query-sized exchange).  Per row, over the partials p in ascending order:
  *   M = max_p LSE_p, LSE = M + log sum_p exp(LSE_p - M), O = sum_p exp(LSE_p - LSE) O_p,

@@ -214,6 +214,16 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t) {
   return hipSuccess;
 }
 
+// The no-allocation scratch: a host buffer of the declared size stands in for the
+// device array, so the layouts of bsx_attn_fwd_noalloc are checked against its bounds.
+static std::vector<char> g_scratch(BSX_NOALLOC_SCRATCH_BYTES);
+void* noalloc_scratch(hipError_t* err) {
+  *err = hipSuccess;
+  g_exp.ws = g_scratch.data();
+  g_exp.ws_bytes = g_scratch.size();
+  return g_scratch.data();
+}
+
 }  // namespace bsx
 
 // ---------------------------------------------------------------- helpers
@@ -360,6 +370,15 @@ int main() {
                        static_cast<float*>(D), static_cast<float*>(D), ws.p(), need, nullptr);
       CHECK(st == BSX_OK);
     }
+    if (n <= BSX_NOALLOC_MAX_CHUNKS && c.n_slots <= BSX_NOALLOC_MAX_CHUNKS) {
+      // the same forward without a workspace, in the fixed scratch
+      const int before = g_exp.n_fwd_calls;
+      const bsx_status st =
+          bsx_attn_fwd_noalloc(&s, D, D, D, D, D, static_cast<int64_t*>(D),
+                               static_cast<int64_t*>(D), &c, static_cast<float*>(D),
+                               static_cast<float*>(D), nullptr);
+      CHECK(st == BSX_OK && (nb == 0 || g_exp.n_fwd_calls == before + 1));
+    }
     if (dtype == BSX_BF16) {  // backward
       const size_t need = bsx_bwd_workspace(&s, &c);
       Buf ws(need);
@@ -393,6 +412,13 @@ int main() {
     CHECK(g_exp.n_fwd_calls == before);
     CHECK(bsx_lse_merge(129, 10, 128, static_cast<float*>(D), static_cast<float*>(D), BSX_BF16,
                         D, static_cast<float*>(D), nullptr) == BSX_E_UNSUPPORTED);
+    bsx_chunks big;
+    random_chunks(100000, BSX_NOALLOC_MAX_CHUNKS + 1, 4, true, &big);
+    s.ctx_len = 100000;
+    CHECK(bsx_attn_fwd_noalloc(&s, D, D, D, nullptr, nullptr, static_cast<int64_t*>(D),
+                               static_cast<int64_t*>(D), &big, static_cast<float*>(D),
+                               static_cast<float*>(D), nullptr) == BSX_E_UNSUPPORTED);
+    CHECK(g_exp.n_fwd_calls == before);
   }
 
   if (g_fail) {
