@@ -191,6 +191,26 @@ def test_backward_training_workload_all_heads():
     assert np.all(dk[tail:] == 0) and np.all(dv[tail:] == 0)
 
 
+def test_backward_rank_share_sorted_chunks():
+    """One rank's chunks listed in position order, no self keys; some blocks' ranges fall
+    between the chunks (their rows see none of the local keys)."""
+    wl = custom_workload(seed=15, ctx_len=8192, n_q_heads=32, n_kv_heads=8, block_size=16,
+                         anchor=[0, 900, 3000, 5000, 8192, 6100, 2100], ctx_begin=[0] * 7,
+                         chunk_start=[1024, 4096, 7168], chunk_len=[1024, 1024, 1024],
+                         backward=True)
+    k_loc, v_loc = wl.kv_chunks()
+    chunks = bsx.Chunks(wl.chunk_start, wl.chunk_len, [0, 0, 0], 1)
+    dq, dk, dv, dks, dvs = _gpu_forward_backward(wl, k_loc, v_loc, chunks, with_self=False)
+    o_p, lse_p = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                      wl.ctx_begin, 16, wl.chunk_start, wl.chunk_len, [0, 0, 0],
+                                      1, with_self=False)
+    r = oracle.attention_backward(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, 16, wl.chunk_start, wl.chunk_len, wl.d_o,
+                                  np.nan_to_num(o_p[0]), lse_p[0], with_self=False)
+    for name, got, ref in zip(["dq", "dk", "dv"], [dq, dk, dv], r[:3]):
+        _check(name, got, ref)
+
+
 def test_backward_is_deterministic():
     wl = custom_workload(seed=13, ctx_len=2048, n_q_heads=16, n_kv_heads=4, block_size=16,
                          anchor=[700, 2048, 1500], ctx_begin=[0, 0, 0], chunk_start=[0, 1024],
