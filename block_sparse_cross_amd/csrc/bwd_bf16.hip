@@ -147,7 +147,7 @@ constexpr int WIN = 128;      // draft blocks compacted per window
 constexpr int XP_BYTES = 2048;  // one pair's P of one step: [u][lane] x 16 bytes
 constexpr int SEARCH_LDS = 256;  // chunk tables up to this size are searched in LDS
 
-// One stage.  Slot c of row r holds global chunk c ^ (r & 15), so the b128 row reads
+// One stage.  Slot c of row r holds global chunk c ^ swz(r), so the b128 row reads
 // and the transpose reads of the operands are free of bank conflicts.
 struct DkdvStage {
   char q[RS * ROW_B];
@@ -172,6 +172,13 @@ __device__ inline void lds_barrier() {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS chunk swizzle of staged row r: slot c of the row holds global chunk c ^ swz(r).
+// The LDS serves 64 banks of 4 bytes: a b128 operand read covers 16 rows at one chunk
+// (conflict-free when swz is a bijection on r mod 16) and a transpose read 4 aligned
+// rows x 4 adjacent chunks (conflict-free when bits 2-3 of swz differ over the 4
+// rows); the low 4 bits of r rotated by two satisfy both.
+__device__ inline int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // The P exchange.  Written as LDS instructions the compiler does not track: it
 // would otherwise make every access to these buffers (which no direct-to-LDS load
@@ -379,7 +386,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
   // operand reads of a stage: b128 row read of row col, chunk 2 i + half, at
   // (k_rd ^ 32 i); transpose read of rows 16 u + 8 hi + 4 half + tj / 4, chunk
   // 4 db + c0, at (tr_rd[hi] ^ 64 db) + 4096 u
-  const int k_rd = col * ROW_B + 16 * (half ^ (col & 15));
+  const int k_rd = col * ROW_B + 16 * (half ^ swz(col));
   int tr_rd[2];
   {
     const int tj = lane & 15, tg = lane >> 4;
@@ -387,13 +394,14 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
     for (int hi2 = 0; hi2 < 2; ++hi2) {
       const int rr = 8 * hi2 + 4 * half + (tj >> 2);
       const int c0 = 2 * (tg & 1) + ((tj & 3) >> 1);
-      tr_rd[hi2] = rr * ROW_B + 16 * (c0 ^ rr) + 8 * (tj & 1);
+      tr_rd[hi2] = rr * ROW_B + 16 * (c0 ^ swz(rr)) + 8 * (tj & 1);
     }
   }
   // staging: wave w fills rows 8 w .. 8 w + 7 of Q and of dO, four rows per load
-  // (lane: row 8 w + 4 i + lane / 16, slot lane % 16 <- chunk slot ^ (row & 15));
+  // (lane: row 8 w + 4 i + lane / 16, slot lane % 16 <- chunk slot ^ swz(row), where
+  // swz(row) = ((lane / 16) << 2) | (2 (w & 1) + i));
   // wave 0 also loads the 32 rows' statistics (lane: row lane % 32, field lane / 32)
-  const uint32_t ld_chunk = uint32_t(((lane & 15) ^ (8 * (wave & 1)) ^ (lane >> 4)) * 16);
+  const uint32_t ld_chunk = uint32_t(((lane & 15) ^ ((lane >> 4) << 2) ^ (2 * (wave & 1))) * 16);
   const int blk_elems = B * Hq * D;
   const uint32_t blk_bytes = uint32_t(blk_elems) * 2u;
   const uint32_t blk_stat_bytes = uint32_t(B * Hq) * 8u;
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
         const int rr = isub * RS + 8 * wave + 4 * i + (lane >> 4);  // row within the block
         const int qq = rr / G;
         const uint32_t off = rr < nr ? uint32_t(((qq * Hq + g * G + (rr - qq * G)) * D) * 2) +
-                                           (ld_chunk ^ uint32_t(64 * i))
+                                           (ld_chunk ^ uint32_t(16 * i))
                                      : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             qr, (lds_void*)(dst.q + (8 * wave_u + 4 * i) * ROW_B), 16, off, 0, 0, 0);
@@ -706,12 +714,13 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
   const int64_t gofs = int64_t(g) * D;
   // Direct-to-LDS staging: wave w fills rows 16w .. 16w + 15 of a tile, four rows per
   // instruction, one 16-byte chunk per lane; slot c of LDS row r holds global chunk
-  // c ^ (r & 15), so the b128 and transpose operand reads below are conflict-free.
+  // c ^ swz(r), so the b128 and transpose operand reads below are conflict-free.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ld_row_off = uint32_t(16 * wave + (lane >> 4)) * row_bytes;
-  const uint32_t ld_chunk = uint32_t(((lane & 15) ^ (lane >> 4)) * 16);
+  // (row 16w + 4i + lane / 16: swz = ((lane / 16) << 2) | i)
+  const uint32_t ld_chunk = uint32_t(((lane & 15) ^ ((lane >> 4) << 2)) * 16);
   // b128 read of key row col [+32], chunk 2t + half: address (k_rd ^ 32t) [+ 8192]
-  const int k_rd = col * ROW_BYTES + 16 * (half ^ (col & 15));
+  const int k_rd = col * ROW_BYTES + 16 * (half ^ swz(col));
   // transpose read (rows 16u + 8hi + 4half + j/4, chunk 4db + c0): (tr_rd[hi] ^ 64db) + 4096u
   const int tj = lane & 15, tg = lane >> 4;
   int tr_rd[2];
@@ -719,7 +728,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
   for (int hi2 = 0; hi2 < 2; ++hi2) {
     const int rr = 8 * hi2 + 4 * half + (tj >> 2);
     const int c0 = 2 * (tg & 1) + ((tj & 3) >> 1);
-    tr_rd[hi2] = rr * ROW_BYTES + 16 * (c0 ^ rr) + 8 * (tj & 1);
+    tr_rd[hi2] = rr * ROW_BYTES + 16 * (c0 ^ swz(rr)) + 8 * (tj & 1);
   }
 
   // phase 0: local context chunks; phase 1: the draft blocks' own keys
@@ -844,7 +853,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
       const __amdgpu_buffer_rsrc_t vb = make_rsrc(vbase + l0 * kstride + gofs, bytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t off = ld_row_off + uint32_t(4 * i) * row_bytes + (ld_chunk ^ uint32_t(64 * i));
+        const uint32_t off = ld_row_off + uint32_t(4 * i) * row_bytes + (ld_chunk ^ uint32_t(16 * i));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             kb, (lds_void*)(kdst + (16 * wave_u + 4 * i) * ROW_BYTES), 16, off, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
