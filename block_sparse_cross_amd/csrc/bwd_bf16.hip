@@ -180,6 +180,20 @@ typedef __attribute__((address_space(3))) void lds_void;
 // rows); the low 4 bits of r rotated by two satisfy both.
 __device__ inline int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// x / G for the query-head group size G and 0 <= x < 2^32 / G: the high word of
+// x * ceil(2^32 / G).  With ceil(2^32 / G) = (2^32 + e) / G, 0 <= e < G, the product
+// adds x e / 2^32 < 1 to x / G's fractional part, which stays below 1 (G = 1 apart).
+struct DivByG {
+  uint32_t m;
+  bool one;
+  __device__ explicit DivByG(int G)
+      : m(G > 1 ? uint32_t(((uint64_t(1) << 32) + uint64_t(G) - 1) / uint64_t(G)) : 0u),
+        one(G == 1) {}
+  __device__ int operator()(int x) const {
+    return one ? x : int(__umulhi(uint32_t(x), m));
+  }
+};
+
 // The P exchange.  Written as LDS instructions the compiler does not track: it
 // would otherwise make every access to these buffers (which no direct-to-LDS load
 // targets) wait for all direct-to-LDS prefetches in flight.  The writes complete
@@ -402,6 +416,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
   // swz(row) = ((lane / 16) << 2) | (2 (w & 1) + i));
   // wave 0 also loads the 32 rows' statistics (lane: row lane % 32, field lane / 32)
   const uint32_t ld_chunk = uint32_t(((lane & 15) ^ ((lane >> 4) << 2) ^ (2 * (wave & 1))) * 16);
+  const DivByG div_g(G);  // rows of a block are < B G, far below 2^32 / G
   const int blk_elems = B * Hq * D;
   const uint32_t blk_bytes = uint32_t(blk_elems) * 2u;
   const uint32_t blk_stat_bytes = uint32_t(B * Hq) * 8u;
@@ -442,7 +457,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int rr = isub * RS + 8 * wave + 4 * i + (lane >> 4);  // row within the block
-        const int qq = rr / G;
+        const int qq = div_g(rr);
         const uint32_t off = rr < nr ? uint32_t(((qq * Hq + g * G + (rr - qq * G)) * D) * 2) +
                                            (ld_chunk ^ uint32_t(16 * i))
                                      : 0x80000000u;
@@ -454,7 +469,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
       if (wave_u == 0) {
         const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.stats + q0 * Hq * 2, blk_stat_bytes);
         const int rr = isub * RS + col;
-        const int qq = rr / G;
+        const int qq = div_g(rr);
         const uint32_t off =
             rr < nr ? uint32_t(((qq * Hq + g * G + (rr - qq * G)) * 2 + half) * 4) : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void*)(dst.lse2), 4, off, 0, 0, 0);
@@ -470,7 +485,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
     // its middle publishes A's P (buffer `xpb`) and the stage of step j + 1.
     auto step = [&](DkdvStage& cur, DkdvStage& nx, char* xpb) -> bool {
       char* xpp = xpb + pair * XP_BYTES;
-      f32x16 s = zero16();
+      f32x16 s;  // set in the role that is live (a zero start in its first product)
       bf16x8 pb[2];
       bf16x4 tr[2][4][2];  // phase-2 transpose operands, read before the barrier
       float4 st4[4];       // A: log2 LSE (+inf for an invisible key); B: D
@@ -483,6 +498,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
         for (int a = 0; a < 4; ++a)
           st4[a] = *reinterpret_cast<const float4*>(cur.lse2 + 8 * a + 4 * half);
         __builtin_amdgcn_sched_barrier(0);
+        s = zero16();
 #pragma unroll
         for (int i = 0; i < 8; ++i) s = mfma_bf16(as_bf16x8(opd[i]), kf[i], s);
         __builtin_amdgcn_sched_barrier(0);
@@ -517,6 +533,7 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
         for (int i = 0; i < 8; ++i)
           opd[i] = *reinterpret_cast<const u32x4*>(cur.d_o + (k_rd ^ (32 * i)));
         __builtin_amdgcn_sched_barrier(0);
+        s = zero16();
 #pragma unroll
         for (int i = 0; i < 8; ++i) s = mfma_bf16(as_bf16x8(opd[i]), kf[i], s);
         __builtin_amdgcn_sched_barrier(0);
