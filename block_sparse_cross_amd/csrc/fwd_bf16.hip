@@ -52,6 +52,18 @@ constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;
 
+// The two values of a query row held by lanes l and l ^ 32, as (a, b) in either order:
+// v_permlane32_swap exchanges the upper half-wave of its first operand with the lower
+// half-wave of its second, so with two copies of x every lane ends up holding x of
+// both half-waves.  A VALU exchange, unlike a shuffle through LDS (ds_bpermute), which
+// would queue behind the tile's operand reads.
+__device__ inline void half_pair(float x, float* a, float* b) {
+  float u = x, w = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(u), "+v"(w));
+  *a = u;
+  *b = w;
+}
+
 struct Tile {
   int64_t p0;     // first position
   int64_t l0;     // local row of p0
@@ -345,7 +357,11 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[b2][v]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
+    {
+      float ma, mb;
+      half_pair(mt, &ma, &mb);
+      mt = fmaxf(ma, mb) * c2;
+    }
     // Lazy rescale: keep the reference max until a tile exceeds it by more than
     // kRescaleSlack (base 2), so exp2 results stay <= 2^kRescaleSlack and the
     // accumulator is rescaled only when the reference moves.
@@ -400,7 +416,9 @@ __global__ __launch_bounds__(THREADS, 2) void fwd_bf16_kernel(FwdParams, int n_t
   // 32 rows in a 16 KB piece of the (now idle) stages, row r's 16-byte chunk c at slot
   // c ^ r (conflict-free lane-per-row writes and row-per-32-lanes reads), with each
   // row's destination next to them (-1: a row without keys, whose O is not written).
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  float la, lb;
+  half_pair(lsum, &la, &lb);
+  const float ltot = la + lb;
   const bool has_keys = row_ok && live && ltot > 0.f;
   const float lse_out = has_keys ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
   if (row_ok && half == 0) {
