@@ -1114,12 +1114,18 @@ __global__ __launch_bounds__(PLAN_THREADS) void bwd_dq_plan_kernel(BwdParams, in
 }
 
 // ---------------------------------------------------------------- dQ reduce
-// dQ of a split row tile = scale * sum of its pieces' partials, in piece order.
-// One workgroup per (split row tile, KV head, 32-row group); partials are read once.
-constexpr int RED_ROWS = 32;
+// dQ of a split row tile = scale * sum of its pieces' partials.  One workgroup per
+// (split row tile, KV head, 8-row group): its four 64-lane groups each add a fixed
+// quarter of the pieces in piece order, and the four sums are added in group order,
+// so the result is deterministic.  A long walk splits into many pieces (tens), and
+// one lane adding all of them one after another would set the kernel's time.
+constexpr int RED_ROWS = 8;
+constexpr int RED_SPLIT = THREADS / (RED_ROWS * 8);  // lane groups per row group
 
 __global__ __launch_bounds__(THREADS) void bwd_dq_reduce_kernel(BwdParams, int n_tiles, int cap) {
   const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  __shared__ f32x4v s_part[RED_SPLIT - 1][RED_ROWS * 8][4];
   const int Hkv = p.n_kv_heads, Hq = p.n_q_heads, G = Hq / Hkv;
   constexpr int kGroups = QROWS / RED_ROWS;
   const int g = blockIdx.x % Hkv;
@@ -1132,20 +1138,34 @@ __global__ __launch_bounds__(THREADS) void bwd_dq_reduce_kernel(BwdParams, int n
   const int32_t* multi_tile = sbase + n_tiles + 2 * int64_t(cap);
   const int t = multi_tile[m];
   const int c = count[t], s0 = sbase[t];
-  const int row = rg * RED_ROWS + (threadIdx.x >> 3), d0 = (threadIdx.x & 7) * 16;
+  const int k = threadIdx.x / (RED_ROWS * 8);  // lane group: pieces [c k / 4, c (k + 1) / 4)
+  const int li = threadIdx.x % (RED_ROWS * 8);
+  const int row = rg * RED_ROWS + (li >> 3), d0 = (li & 7) * 16;
   const int64_t r = int64_t(t) * QROWS + row;
   const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
-  if (r >= n_rows) return;
-  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  const bool row_ok = r < n_rows;
   f32x4v acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < c; ++j) {
-    const float* src = p.dq_part + ((int64_t(s0 + j) * Hkv + g) * QROWS + row) * D + d0;
+  const int j0 = c * k / RED_SPLIT, j1 = c * (k + 1) / RED_SPLIT;
+  if (row_ok) {
+    for (int j = j0; j < j1; ++j) {
+      const float* src = p.dq_part + ((int64_t(s0 + j) * Hkv + g) * QROWS + row) * D + d0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc[i] += __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(src) + i);
+      for (int i = 0; i < 4; ++i)
+        acc[i] += __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(src) + i);
+    }
   }
+  if (k > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_part[k - 1][li][i] = acc[i];
+  }
+  __syncthreads();
+  if (k > 0 || !row_ok) return;
+#pragma unroll
+  for (int q = 0; q < RED_SPLIT - 1; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += s_part[q][li][i];
   const int64_t qi = r / G;
   const int h = g * G + int(r % G);
   float* dst = p.dq + (qi * Hq + h) * D + d0;
