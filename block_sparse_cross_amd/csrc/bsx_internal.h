@@ -190,9 +190,12 @@ hipError_t launch_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
                             const float* o_parts, const float* lse_parts, bool out_bf16,
                             void* o_out, float* lse_out, hipStream_t stream);
 // dQ work split: the row tiles (kDqRows query rows of one KV head) are cut into
-// pieces of P key tiles, P chosen so the launch has about kDqTargetWgs workgroups.
+// pieces of P key tiles, P chosen so the launch has about kDqTargetWgs workgroups:
+// about 1.75 rounds of the chip's 512 dQ workgroup slots (two per CU).  Fewer, longer
+// pieces pay fewer workgroup prologues and leave fewer partials to write and reduce;
+// a count just past a whole number of rounds leaves a thin last round.
 constexpr int kDqRows = 128;
-constexpr int kDqTargetWgs = 2048;
+constexpr int kDqTargetWgs = 896;
 constexpr int kDqMinPieceTiles = 8;
 struct DqLayout {
   int64_t n_tiles;        // row tiles per KV head
