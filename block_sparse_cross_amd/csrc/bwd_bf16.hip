@@ -1125,7 +1125,7 @@ constexpr int RED_SPLIT = THREADS / (RED_ROWS * 8);  // lane groups per row grou
 __global__ __launch_bounds__(THREADS) void bwd_dq_reduce_kernel(BwdParams, int n_tiles, int cap) {
   const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
   typedef float f32x4v __attribute__((ext_vector_type(4)));
-  __shared__ f32x4v s_part[RED_SPLIT - 1][RED_ROWS * 8][4];
+  __shared__ f32x4v s_part[RED_SPLIT - 1][4][RED_ROWS * 8];  // lane-minor: conflict-free
   const int Hkv = p.n_kv_heads, Hq = p.n_q_heads, G = Hq / Hkv;
   constexpr int kGroups = QROWS / RED_ROWS;
   const int g = blockIdx.x % Hkv;
@@ -1158,14 +1158,14 @@ __global__ __launch_bounds__(THREADS) void bwd_dq_reduce_kernel(BwdParams, int n
   }
   if (k > 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_part[k - 1][li][i] = acc[i];
+    for (int i = 0; i < 4; ++i) s_part[k - 1][i][li] = acc[i];
   }
   __syncthreads();
   if (k > 0 || !row_ok) return;
 #pragma unroll
   for (int q = 0; q < RED_SPLIT - 1; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += s_part[q][li][i];
+    for (int i = 0; i < 4; ++i) acc[i] += s_part[q][i][li];
   const int64_t qi = r / G;
   const int h = g * G + int(r % G);
   float* dst = p.dq + (qi * Hq + h) * D + d0;
