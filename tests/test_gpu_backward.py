@@ -86,6 +86,14 @@ CASES = {
     # 64-key tiles spanning distant chunks; rows 64..127 (positions 2024..2087) are seen
     # by no block, so their dK/dV must be exactly zero
     "split_tiles_unseen": (3000, 8, 2, 16, [20, 2010], None, [0, 2000, 900], [40, 100, 30]),
+    # query-head groups that do not divide the 32-row steps or 128-row tiles (a block's
+    # rows end inside a step, a query's heads straddle tiles), odd block sizes
+    "gqa3_block7": (1800, 6, 2, 7, [0, 5, 900, 1799, 1800, 333, 1200], None,
+                    [0, 600, 1200], [600, 600, 600]),
+    "gqa5_block13": (1000, 10, 2, 13, [1000, 1, 500, 999, 250], None,
+                     [0, 250, 500, 750], [250, 250, 250, 250]),
+    "gqa7_block33": (2100, 7, 1, 33, [2100, 64, 1000, 2099], [0, 0, 500, 1000],
+                     [100, 1100], [1000, 1000]),
 }
 
 

@@ -327,6 +327,16 @@ EDGE_CASES = {
     # in position order)
     "unsorted_slot": (3000, 8, 2, 16, [0, 1, 777, 2999, 3000, 1999], None,
                       [2000, 0, 1000, 2500], [500, 1000, 1000, 500], [0, 0, 0, 1], 2),
+    # query-head groups that do not divide a 32- or 128-row tile (a block's rows and a
+    # query's heads straddle tiles), with odd block sizes
+    "gqa3_block7": (1800, 6, 2, 7, [0, 5, 900, 1799, 1800, 333, 1200], None,
+                    [0, 600, 1200], [600, 600, 600], [0, 1, 0], 2),
+    "gqa5_block3": (1000, 10, 2, 3, [1000, 1, 500, 999, 250, 750, 0, 100, 900], None,
+                    [0, 250, 500, 750], [250, 250, 250, 250], None, None),
+    "gqa7_block33": (2100, 7, 1, 33, [2100, 64, 1000, 2099], [0, 0, 500, 1000],
+                     [0, 1100], [1100, 1000], None, None),
+    "gqa6_block20": (1500, 12, 2, 20, [1500, 700, 20, 1499, 300], [0, 0, 0, 700, 0],
+                     [0, 500, 1000], [500, 500, 500], [1, 0, 1], 2),
 }
 
 
