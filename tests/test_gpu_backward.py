@@ -229,3 +229,34 @@ def test_backward_is_deterministic():
     b = _gpu_forward_backward(wl, k_loc, v_loc, chunks)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_backward_custom_scale():
+    """A softmax scale other than 1/sqrt(d) (0.3) in both passes: P, dS and the scale of dQ
+    and dK all follow it (GQA 3, block size 10)."""
+    cs, cl = [0, 700, 1400], [700, 700, 600]
+    wl = custom_workload(seed=41, ctx_len=2000, n_q_heads=6, n_kv_heads=2, block_size=10,
+                         anchor=[2000, 350, 1500, 0], ctx_begin=[0, 0, 200, 0], chunk_start=cs,
+                         chunk_len=cl, backward=True)
+    k_loc, v_loc = wl.kv_chunks()
+    dev = upload(wl, k_loc, v_loc)
+    shape = shape_of(wl)
+    shape.scale = 0.3
+    chunks = bsx.Chunks(cs, cl)
+    log("backward, scale 0.3")
+    o_part, lse_part = run_fwd(shape, dev["q"], dev["k"], dev["v"], dev["k_self"],
+                               dev["v_self"], dev["anchor"], dev["ctx_begin"], chunks)
+    o, lse = run_merge(o_part, lse_part)
+    grads = run_bwd(shape, dev["q"], dev["k"], dev["v"], dev["k_self"], dev["v_self"], o, lse,
+                    dev["d_o"], dev["anchor"], dev["ctx_begin"], chunks)
+    torch.cuda.synchronize()
+    ro, rl = oracle.slot_partials(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, 10, np.asarray(cs), np.asarray(cl),
+                                  np.zeros(len(cs), np.int64), 1, scale=0.3)
+    nq, hq = wl.q.shape[0], 6
+    mo, ml = oracle.lse_merge(ro.reshape(2, nq * hq, -1), rl.reshape(2, nq * hq))
+    r = oracle.attention_backward(wl.q, k_loc, v_loc, wl.k_self, wl.v_self, wl.anchor,
+                                  wl.ctx_begin, 10, np.asarray(cs), np.asarray(cl), wl.d_o,
+                                  mo.reshape(nq, hq, -1), ml.reshape(nq, hq), scale=0.3)
+    for name, got, ref in zip(["dq", "dk", "dv", "dk_self", "dv_self"], grads, r):
+        _check(name, got.cpu().numpy(), ref)
