@@ -337,6 +337,11 @@ EDGE_CASES = {
                      [0, 1100], [1100, 1000], None, None),
     "gqa6_block20": (1500, 12, 2, 20, [1500, 700, 20, 1499, 300], [0, 0, 0, 700, 0],
                      [0, 500, 1000], [500, 500, 500], [1, 0, 1], 2),
+    # 300 chunks in 3 slots: the chunk table (4.8 KB) is uploaded to the workspace
+    # instead of riding in the kernel arguments
+    "many_chunks_uploaded": (4800, 8, 2, 16, [30, 4800, 2400, 1111, 4000, 16], None,
+                             list(range(0, 4800, 16)), [16] * 300,
+                             [(7 * i) % 3 for i in range(300)], 3),
 }
 
 
