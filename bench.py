@@ -10,9 +10,10 @@ pipelined as a training loop runs them: each batch is planned (cost kernel and c
 readback on a second stream, then the host LPT) while the previous batch's attention
 runs, so every timed step does one whole plan and one whole attention pass.  The
 default workload is the largest one that runs the whole path, forward and backward:
-the packed training step (8 samples packed into 131072 keys, H_q = 32, H_kv = 8,
-d = 128, one anchor per 1024 tokens of a sample with 16 draft queries each, 128 KV
-chunks of 1024 balanced by LPT over 16 bins, plus the draft blocks' own keys).
+the packed training step (8 samples packed into 131072 keys, the tail past them
+padding that no query sees, H_q = 32, H_kv = 8, d = 128, one anchor per 1024 tokens of
+a sample with 16 draft queries each, 128 KV chunks of 1024 balanced by LPT over 16
+bins, plus the draft blocks' own keys).
 
 Prints one JSON line: useful TFLOP/s (masked-out and padded work excluded) of the
 step; a roofline object for the dominant call (the backward on the training step,
