@@ -94,6 +94,9 @@ CASES = {
                      [0, 250, 500, 750], [250, 250, 250, 250]),
     "gqa7_block33": (2100, 7, 1, 33, [2100, 64, 1000, 2099], [0, 0, 500, 1000],
                      [100, 1100], [1000, 1000]),
+    # 2100 chunks of 2 keys: more entries than the dQ plan keeps in LDS
+    "many_tiny_chunks": (4200, 4, 2, 4, [0, 4200, 2100, 1, 3333, 777], None,
+                         list(range(0, 4200, 2)), [2] * 2100),
 }
 
 

@@ -342,6 +342,10 @@ EDGE_CASES = {
     "many_chunks_uploaded": (4800, 8, 2, 16, [30, 4800, 2400, 1111, 4000, 16], None,
                              list(range(0, 4800, 16)), [16] * 300,
                              [(7 * i) % 3 for i in range(300)], 3),
+    # 2100 chunks of 2 keys in 4 slots: more entries than the launch-order pass and the
+    # dQ plan keep in LDS (the table is read from memory)
+    "many_tiny_chunks": (4200, 4, 2, 4, [0, 4200, 2100, 1, 3333, 777], None,
+                         list(range(0, 4200, 2)), [2] * 2100, [i % 4 for i in range(2100)], 4),
 }
 
 
