@@ -1,8 +1,9 @@
-"""GPU parity with many draft blocks against the fp64 oracle: more blocks than one window
-of the dK/dV kernel's block compaction (128), than the row-statistics kernel stages in
-LDS per pass (1024) and than the launch-order pass keeps in LDS (1024), so the paths
-that walk blocks in several windows or read their ranges from memory run.  Small heads
-and blocks keep the oracle fast."""
+"""GPU parity with many draft blocks or items against the fp64 oracle: more blocks than
+one window of the dK/dV kernel's block compaction (128), than the row-statistics kernel
+stages in LDS per pass (1024) and than the launch-order pass keeps in LDS (1024), so the
+paths that walk blocks in several windows or read their ranges from memory run; and more
+(row tile, output) items than the launch-order pass sorts, so the forward launches in
+its natural order.  Small heads and blocks keep the oracle fast."""
 import numpy as np
 import pytest
 import torch
@@ -105,3 +106,35 @@ def test_backward_many_blocks(n_blocks):
                                   mo.reshape(nq, hq, -1), ml.reshape(nq, hq))
     for name, got, ref in zip(["dq", "dk", "dv", "dk_self", "dv_self"], grads, r):
         _check_grad(name, got.cpu().numpy(), ref)
+
+
+def test_forward_more_items_than_the_launch_order_pass_takes():
+    """32768 one-key slots and the self slot over one row tile: 32769 (row tile, output)
+    items, more than the launch-order pass sorts (32768), so the forward launches in its
+    natural order.  Every partial against the oracle's attention over its one key."""
+    n_keys = 32768
+    anchor, begin = [n_keys, 12345], [0, 10000]
+    wl = custom_workload(seed=70, ctx_len=n_keys, n_q_heads=1, n_kv_heads=1, block_size=1,
+                         anchor=anchor, ctx_begin=begin, chunk_start=list(range(n_keys)),
+                         chunk_len=[1] * n_keys)
+    k_loc, v_loc = wl.kv_chunks()
+    dev = upload(wl, k_loc, v_loc)
+    chunks = bsx.Chunks(np.arange(n_keys), np.ones(n_keys, np.int64))
+    log("forward, 32769 items")
+    o, lse = run_fwd(shape_of(wl), dev["q"], dev["k"], dev["v"], dev["k_self"], dev["v_self"],
+                     dev["anchor"], dev["ctx_begin"], chunks)
+    scale = oracle.default_scale(128)
+    ro = np.full((n_keys + 1, 2, 1, 128), np.nan)
+    rl = np.full((n_keys + 1, 2, 1), np.nan)
+    for b in range(2):
+        q = wl.q[b:b + 1, 0]
+        for s in range(n_keys):
+            if begin[b] <= s < anchor[b]:
+                ob, lb = oracle.partial_attention(q, k_loc[s:s + 1, 0], v_loc[s:s + 1, 0], scale)
+                ro[s, b, 0], rl[s, b, 0] = ob[0], lb[0]
+            else:
+                rl[s, b, 0] = -np.inf
+        ob, lb = oracle.partial_attention(q, wl.k_self[b:b + 1, 0], wl.v_self[b:b + 1, 0], scale)
+        ro[n_keys, b, 0], rl[n_keys, b, 0] = ob[0], lb[0]
+    tol_o, tol_l = tolerances("bf16")
+    compare_partials(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_o, tol_l, "partials")
