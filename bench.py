@@ -266,8 +266,7 @@ def time_forward(step: Step, reps: int):
 
 
 FWD_KERNELS = ["fwd_order_kernel", "fwd_bf16_kernel", "fwd_piece_merge_kernel (split launches)"]
-BWD_KERNELS = ["bwd_delta_kernel", "bwd_dkdv_kernel", "bwd_dq_plan_kernel", "bwd_dq_kernel",
-               "bwd_dq_reduce_kernel"]
+BWD_KERNELS = ["bwd_delta_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "bwd_dq_reduce_kernel"]
 
 
 def fwd_roofline(step: Step, reps: int, workload: str) -> dict:

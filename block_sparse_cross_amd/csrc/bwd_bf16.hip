@@ -10,7 +10,8 @@
 // subset (one rank's local keys) this gives exact local dK/dV and that share of dQ.
 //
 // Three kernels, no atomics (results are deterministic):
-//   delta: D_r = rowsum(dO * O), stored with the row's log2-domain LSE.
+//   delta: D_r = rowsum(dO * O), stored with the row's log2-domain LSE; the same
+//          launch flags the key tiles no draft block sees and plans the dQ split.
 //   dkdv:  key-major.  A workgroup owns 64 local keys of one KV head, 32 per wave
 //          pair, and walks the draft blocks whose range reaches its keys, 32 query
 //          rows at a time streamed into LDS.  In a pair one wave computes P and dV,
@@ -21,8 +22,8 @@
 //          rows are their block's.
 //   dq:    query-major, shaped like the forward kernel: 128 rows per workgroup,
 //          K/V tiles of 64 keys in LDS; S^T = K Q^T and dP^T = V dO^T put rows in
-//          lane columns, dQ^T += K^T dS^T reads K^T with transpose loads.  A
-//          planning pass cuts each row tile's key walk into pieces of P tiles (about
+//          lane columns, dQ^T += K^T dS^T reads K^T with transpose loads.  The
+//          plan cuts each row tile's key walk into pieces of P tiles (about
 //          kDqTargetWgs workgroups in all: draft blocks see very different context
 //          lengths); a row tile of one piece writes dQ directly, the pieces of a split
 //          row tile write partial sums that a reduce kernel adds in piece order.
@@ -41,6 +42,8 @@ namespace {
 constexpr int D = 128;
 constexpr int THREADS = 256;
 constexpr int KV_KEYS = 64;   // keys per dK / dV workgroup (and per flagged key tile)
+constexpr int QROWS = kDqRows;  // query rows per dQ workgroup (row tile)
+constexpr int KT = 64;          // keys per dQ K / V tile
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -49,23 +52,192 @@ __device__ inline float row_lse2(float lse) {
   return lse == -INFINITY ? INFINITY : lse * kLog2e;
 }
 
+// ---------------------------------------------------------------- dQ split plan
+// One workgroup, the first of the row-statistics launch (the plan needs only the block
+// ranges and the chunk list, so it costs no launch of its own).  w_t = key tiles of row
+// tile t's context walk (the dQ kernel's own union of its rows' ranges over all local
+// chunks); P = max(kDqMinPieceTiles, ceil(sum w / target)); count_t = max(1,
+// ceil(w_t / P)) pieces.  Pieces are listed row tile by row tile; split row tiles
+// (count_t > 1) get consecutive partial slots from sbase_t.  Header: P, number of
+// pieces, number of split row tiles.
+constexpr int kWaves = THREADS / 64;
+constexpr int PLAN_LDS_TILES = 512;    // plans up to this many row tiles ...
+constexpr int PLAN_LDS_ENTRIES = 512;  // ... and chunks work from LDS
+struct PlanLds {
+  ChunkEntry ent[PLAN_LDS_ENTRIES];
+  int64_t lo[PLAN_LDS_TILES], hi[PLAN_LDS_TILES];
+  int32_t tiles[PLAN_LDS_TILES];
+  int64_t w[kWaves];
+  int scan[3][kWaves];
+};
+
+__device__ void dq_plan_workgroup(const BSX_KARG BwdParams& p, int n_tiles, int cap, int target,
+                                  PlanLds& s) {
+  const int tid = threadIdx.x;
+  const int Hkv = p.n_kv_heads, G = p.n_q_heads / Hkv;
+  const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
+  const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
+  const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table);
+  int32_t* plan = p.dq_plan;
+  int32_t* count = plan + 4;
+  int32_t* sbase = count + n_tiles;
+  int32_t* piece_tile = sbase + n_tiles;
+  int32_t* piece_j = piece_tile + cap;
+  int32_t* multi_tile = piece_j + cap;
+
+  // each thread owns a contiguous run of row tiles
+  const int per = (n_tiles + THREADS - 1) / THREADS;
+  const int t0 = tid * per < n_tiles ? tid * per : n_tiles;
+  const int t1 = t0 + per < n_tiles ? t0 + per : n_tiles;
+  auto span = [&](int t, int64_t* mlo, int64_t* mhi) {
+    const int64_t r0 = int64_t(t) * QROWS;
+    const int64_t r1 = r0 + QROWS < n_rows ? r0 + QROWS : n_rows;
+    row_span_union(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, G, false, r0, r1, mlo, mhi);
+  };
+  int64_t wsum = 0;
+  const bool small = n_tiles <= PLAN_LDS_TILES && p.n_entries <= PLAN_LDS_ENTRIES;
+  if (small) {
+    // small plan: ranges, entries and the walk lengths in LDS
+    for (int e = tid; e < p.n_entries; e += THREADS) s.ent[e] = ent[e];
+    for (int t = tid; t < n_tiles; t += THREADS) {
+      span(t, &s.lo[t], &s.hi[t]);
+      s.tiles[t] = 0;
+    }
+    __syncthreads();
+    if (p.entries_order >= 2) {
+      // sorted and disjoint: a row tile bisects to its first entry ending after its
+      // range starts and walks only the entries its range reaches
+      for (int t = tid; t < n_tiles; t += THREADS) {
+        const int64_t lo = s.lo[t], hi = s.hi[t];
+        if (!(lo < hi)) continue;
+        int e = 0, b = p.n_entries;
+        while (e < b) {
+          const int mid = (e + b) >> 1;
+          if (s.ent[mid].start + int64_t(s.ent[mid].len) > lo) b = mid; else e = mid + 1;
+        }
+        int64_t w = 0;
+        for (; e < p.n_entries && s.ent[e].start < hi; ++e)
+          w += walk_tiles(s.ent, e, e + 1, lo, hi, KT);
+        s.tiles[t] = int32_t(w);
+      }
+    } else {
+      // (row tile, entry) pairs spread over all lanes (at most 2^18 of them here)
+      const int n_pairs = n_tiles * p.n_entries;
+      for (int i = tid; i < n_pairs; i += THREADS) {
+        const int t = i / p.n_entries, e = i - t * p.n_entries;
+        const int64_t w = walk_tiles(s.ent, e, e + 1, s.lo[t], s.hi[t], KT);
+        if (w) atomicAdd(&s.tiles[t], int(w));
+      }
+    }
+    __syncthreads();
+    for (int t = t0; t < t1; ++t) wsum += s.tiles[t];
+  } else {
+    for (int t = t0; t < t1; ++t) {
+      int64_t mlo, mhi;
+      span(t, &mlo, &mhi);
+      const int64_t w = walk_tiles(ent, 0, p.n_entries, mlo, mhi, KT);
+      count[t] = int32_t(w < INT32_MAX ? w : INT32_MAX);
+      wsum += w;
+    }
+  }
+  // W: wave sums, then the sum of the wave totals (one barrier)
+  const int lane = tid & 63, wv = tid >> 6;
+  for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
+  if (lane == 0) s.w[wv] = wsum;
+  __syncthreads();
+  int64_t W = 0;
+  for (int i = 0; i < kWaves; ++i) W += s.w[i];
+  int64_t P = (W + target - 1) / target;
+  P = P < kDqMinPieceTiles ? kDqMinPieceTiles : P;
+
+  int own[3] = {0, 0, 0};  // pieces, partial slots, split row tiles
+  for (int t = t0; t < t1; ++t) {
+    const int64_t w = small ? s.tiles[t] : count[t];
+    const int c = int(w > P ? (w + P - 1) / P : 1);
+    count[t] = c;
+    own[0] += c;
+    own[1] += c > 1 ? c : 0;
+    own[2] += c > 1 ? 1 : 0;
+  }
+  // exclusive scans of the three per-thread totals: inclusive scans within each wave,
+  // then the wave totals (one barrier)
+  int incl[3];
+  for (int k = 0; k < 3; ++k) {
+    incl[k] = own[k];
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl[k], off);
+      if (lane >= off) incl[k] += y;
+    }
+    if (lane == 63) s.scan[k][wv] = incl[k];
+  }
+  __syncthreads();
+  int before[3] = {0, 0, 0}, total[3] = {0, 0, 0};
+  for (int i = 0; i < kWaves; ++i)
+    for (int k = 0; k < 3; ++k) {
+      before[k] += i < wv ? s.scan[k][i] : 0;
+      total[k] += s.scan[k][i];
+    }
+  int at = before[0] + incl[0] - own[0], slot = before[1] + incl[1] - own[1],
+      mi = before[2] + incl[2] - own[2];
+  for (int t = t0; t < t1; ++t) {
+    const int c = count[t];
+    for (int j = 0; j < c; ++j) {
+      piece_tile[at + j] = t;
+      piece_j[at + j] = j;
+    }
+    at += c;
+    if (c > 1) {
+      sbase[t] = slot;
+      slot += c;
+      multi_tile[mi++] = t;
+    } else {
+      sbase[t] = -1;
+    }
+  }
+  if (tid == 0) {
+    plan[0] = int32_t(P);
+    plan[1] = total[0];
+    plan[2] = total[2];
+    plan[3] = 0;
+  }
+}
+
 // ---------------------------------------------------------------- row statistics
-// Workgroups [0, seen_wgs): tile_seen[t] for the 64-key local tiles t, THREADS tiles
-// each: 1 when the context range [ctx_begin, anchor) of some draft block holds the
-// position of one of the tile's keys (a key's gradients are sums over the rows that
-// see it, so an unseen tile's dK and dV are zero).  They come first so that their
-// longer loops overlap the rest.  The other workgroups: stats[r] = (log2-domain LSE,
+// Workgroups [0, plan_wgs) (none or one): the dQ split plan.  The next seen_wgs:
+// tile_seen[t] for the 64-key local tiles t, THREADS tiles each: 1 when the context
+// range [ctx_begin, anchor) of some draft block holds the position of one of the
+// tile's keys (a key's gradients are sums over the rows that see it, so an unseen
+// tile's dK and dV are zero).  These come first so that their longer chains of loads
+// overlap the rest.  The other workgroups: stats[r] = (log2-domain LSE,
 // D_r = rowsum(dO * O)) of query row r = q * H_q + h.
 constexpr int kSeenLdsBlocks = 1024;  // block ranges staged in LDS per pass
+constexpr int kSeenLdsEntries = 512;  // chunk tables up to this size are read from LDS
+struct SeenLds {
+  int64_t lo[kSeenLdsBlocks], hi[kSeenLdsBlocks];
+  int64_t est[kSeenLdsEntries];
+  uint32_t elen[kSeenLdsEntries], eoff[kSeenLdsEntries];
+};
+union DeltaLds {  // the plan and the tile flags run in different workgroups
+  PlanLds plan;
+  SeenLds seen;
+};
 
 __global__ __launch_bounds__(THREADS) void bwd_delta_kernel(BwdParams, int64_t n_rows,
-                                                            int seen_wgs, int n_ctx_tiles) {
+                                                            int plan_wgs, int seen_wgs,
+                                                            int n_ctx_tiles, int n_tiles, int cap,
+                                                            int target) {
   const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
-  if (int(blockIdx.x) >= seen_wgs) {
+  __shared__ __attribute__((aligned(16))) DeltaLds lds;
+  const int wg = int(blockIdx.x);
+  if (wg < plan_wgs) {
+    dq_plan_workgroup(p, n_tiles, cap, target, lds.plan);
+    return;
+  }
+  if (wg - plan_wgs >= seen_wgs) {
     const float* o = p.o;
     const uint16_t* d_o = static_cast<const uint16_t*>(p.d_o);
     const int64_t row =
-        int64_t(int(blockIdx.x) - seen_wgs) * (THREADS / 32) + (threadIdx.x >> 5);
+        int64_t(wg - plan_wgs - seen_wgs) * (THREADS / 32) + (threadIdx.x >> 5);
     const int c = (threadIdx.x & 31) * 4;
     float acc = 0.f;
     if (row < n_rows) {
@@ -82,24 +254,34 @@ __global__ __launch_bounds__(THREADS) void bwd_delta_kernel(BwdParams, int64_t n
     return;
   }
   // ---- key tile flags
-  __shared__ int64_t s_lo[kSeenLdsBlocks], s_hi[kSeenLdsBlocks];
-  const int t = int(blockIdx.x) * THREADS + int(threadIdx.x);
+  int64_t* s_lo = lds.seen.lo;
+  int64_t* s_hi = lds.seen.hi;
+  int64_t* s_est = lds.seen.est;
+  uint32_t* s_elen = lds.seen.elen;
+  uint32_t* s_eoff = lds.seen.eoff;
+  const int t = (wg - plan_wgs) * THREADS + int(threadIdx.x);
   const bool own = t < n_ctx_tiles;
   const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
   const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table);
+  // a small chunk table is copied to LDS with the first pass's block ranges (one round
+  // trip): the search and the walk below then read no global memory one load at a time
+  const int n_ent = p.n_entries;
+  const bool lds_ent = n_ent <= kSeenLdsEntries;
+  if (lds_ent) {
+    for (int e = threadIdx.x; e < n_ent; e += THREADS) {
+      s_est[e] = ent[e].start;
+      s_elen[e] = ent[e].len;
+      s_eoff[e] = ent[e].local_off;
+    }
+  }
+  auto e_start = [&](int e) { return lds_ent ? s_est[e] : ent[e].start; };
+  auto e_len = [&](int e) { return int64_t(lds_ent ? s_elen[e] : ent[e].len); };
+  auto e_off = [&](int e) { return int64_t(lds_ent ? s_eoff[e] : ent[e].local_off); };
   // the tile's key rows [r0, r1) cut into at most a few position segments: the first
   // chunk holding row r0 (local offsets increase along the list) and those after it
   const int64_t r0 = int64_t(t) * KV_KEYS;
   const int64_t r1 = r0 + KV_KEYS < p.n_local ? r0 + KV_KEYS : p.n_local;
   int e0 = 0;
-  if (own) {
-    int lo = 0, hi = p.n_entries - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (int64_t(ent[mid].local_off) <= r0) lo = mid; else hi = mid - 1;
-    }
-    e0 = lo;
-  }
   bool seen = false;
   for (int b0 = 0; b0 < p.n_blocks; b0 += kSeenLdsBlocks) {
     const int nb = p.n_blocks - b0 < kSeenLdsBlocks ? p.n_blocks - b0 : kSeenLdsBlocks;
@@ -109,13 +291,21 @@ __global__ __launch_bounds__(THREADS) void bwd_delta_kernel(BwdParams, int64_t n
                     &s_hi[i]);
     __syncthreads();
     if (!own || seen) continue;
-    for (int e = e0; e < p.n_entries && !seen; ++e) {
-      const int64_t off = ent[e].local_off, len = ent[e].len;
+    if (b0 == 0) {
+      int lo = 0, hi = n_ent - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (e_off(mid) <= r0) lo = mid; else hi = mid - 1;
+      }
+      e0 = lo;
+    }
+    for (int e = e0; e < n_ent && !seen; ++e) {
+      const int64_t off = e_off(e), len = e_len(e);
       if (off >= r1) break;
       const int64_t a_row = r0 > off ? r0 : off;
       const int64_t z_row = r1 < off + len ? r1 : off + len;
       if (a_row >= z_row) continue;
-      const int64_t a = ent[e].start + (a_row - off), z = ent[e].start + (z_row - off);
+      const int64_t a = e_start(e) + (a_row - off), z = e_start(e) + (z_row - off);
       for (int i = 0; i < nb; ++i)
         if (s_lo[i] < s_hi[i] && s_lo[i] < z && s_hi[i] > a) {
           seen = true;
@@ -635,8 +825,6 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dkdv_kernel(BwdParams, int n_c
 }
 
 // ---------------------------------------------------------------- dQ
-constexpr int QROWS = kDqRows;
-constexpr int KT = 64;
 constexpr int ROW_BYTES = D * 2;         // staged K / V row: 16 chunks of 16 bytes
 constexpr int TILE_BYTES = KT * ROW_BYTES;
 
@@ -991,128 +1179,6 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
   }
 }
 
-// ---------------------------------------------------------------- dQ split plan
-// One workgroup.  w_t = key tiles of row tile t's context walk (the kernel's own
-// union of its rows' ranges over all local chunks); P = max(kDqMinPieceTiles,
-// ceil(sum w / target)); count_t = max(1, ceil(w_t / P)) pieces.  Pieces are listed
-// row tile by row tile; split row tiles (count_t > 1) get consecutive partial slots
-// from sbase_t.  Header: P, number of pieces, number of split row tiles.
-constexpr int PLAN_THREADS = 1024;
-constexpr int PLAN_LDS_TILES = 2048;    // plans up to this many row tiles ...
-constexpr int PLAN_LDS_ENTRIES = 2048;  // ... and chunks work from LDS
-
-__global__ __launch_bounds__(PLAN_THREADS) void bwd_dq_plan_kernel(BwdParams, int n_tiles,
-                                                                   int cap, int target) {
-  const BSX_KARG BwdParams& p = kernel_arg0<BwdParams>();
-  __shared__ int64_t s_w[PLAN_THREADS];
-  __shared__ int s_scan[3][PLAN_THREADS];
-  __shared__ __attribute__((aligned(16))) ChunkEntry s_ent[PLAN_LDS_ENTRIES];
-  __shared__ int64_t s_lo[PLAN_LDS_TILES], s_hi[PLAN_LDS_TILES];
-  __shared__ int32_t s_tiles[PLAN_LDS_TILES];
-  const int tid = threadIdx.x;
-  const int Hkv = p.n_kv_heads, G = p.n_q_heads / Hkv;
-  const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
-  const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
-  const ChunkEntry* ent = reinterpret_cast<const ChunkEntry*>(table);
-  int32_t* plan = p.dq_plan;
-  int32_t* count = plan + 4;
-  int32_t* sbase = count + n_tiles;
-  int32_t* piece_tile = sbase + n_tiles;
-  int32_t* piece_j = piece_tile + cap;
-  int32_t* multi_tile = piece_j + cap;
-
-  // each thread owns a contiguous run of row tiles
-  const int per = (n_tiles + PLAN_THREADS - 1) / PLAN_THREADS;
-  const int t0 = tid * per < n_tiles ? tid * per : n_tiles;
-  const int t1 = t0 + per < n_tiles ? t0 + per : n_tiles;
-  auto span = [&](int t, int64_t* mlo, int64_t* mhi) {
-    const int64_t r0 = int64_t(t) * QROWS;
-    const int64_t r1 = r0 + QROWS < n_rows ? r0 + QROWS : n_rows;
-    row_span_union(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, G, false, r0, r1, mlo, mhi);
-  };
-  int64_t wsum = 0;
-  if (n_tiles <= PLAN_LDS_TILES && p.n_entries <= PLAN_LDS_ENTRIES) {
-    // small plan: ranges and entries in LDS, (row tile, entry) pairs spread over all lanes
-    for (int e = tid; e < p.n_entries; e += PLAN_THREADS) s_ent[e] = ent[e];
-    for (int t = tid; t < n_tiles; t += PLAN_THREADS) {
-      span(t, &s_lo[t], &s_hi[t]);
-      s_tiles[t] = 0;
-    }
-    __syncthreads();
-    const int64_t n_pairs = int64_t(n_tiles) * p.n_entries;
-    for (int64_t i = tid; i < n_pairs; i += PLAN_THREADS) {
-      const int t = int(i / p.n_entries), e = int(i % p.n_entries);
-      const int64_t w = walk_tiles(s_ent, e, e + 1, s_lo[t], s_hi[t], KT);
-      if (w) atomicAdd(&s_tiles[t], int(w));
-    }
-    __syncthreads();
-    for (int t = t0; t < t1; ++t) {
-      count[t] = s_tiles[t];
-      wsum += s_tiles[t];
-    }
-  } else {
-    for (int t = t0; t < t1; ++t) {
-      int64_t mlo, mhi;
-      span(t, &mlo, &mhi);
-      const int64_t w = walk_tiles(ent, 0, p.n_entries, mlo, mhi, KT);
-      count[t] = int32_t(w < INT32_MAX ? w : INT32_MAX);
-      wsum += w;
-    }
-  }
-  s_w[tid] = wsum;
-  __syncthreads();
-  for (int off = PLAN_THREADS / 2; off > 0; off >>= 1) {
-    if (tid < off) s_w[tid] += s_w[tid + off];
-    __syncthreads();
-  }
-  const int64_t W = s_w[0];
-  int64_t P = (W + target - 1) / target;
-  P = P < kDqMinPieceTiles ? kDqMinPieceTiles : P;
-
-  int own[3] = {0, 0, 0};  // pieces, partial slots, split row tiles
-  for (int t = t0; t < t1; ++t) {
-    const int64_t w = count[t];
-    const int c = int(w > P ? (w + P - 1) / P : 1);
-    count[t] = c;
-    own[0] += c;
-    own[1] += c > 1 ? c : 0;
-    own[2] += c > 1 ? 1 : 0;
-  }
-  // exclusive scans of the three per-thread totals
-  for (int k = 0; k < 3; ++k) s_scan[k][tid] = own[k];
-  __syncthreads();
-  for (int off = 1; off < PLAN_THREADS; off <<= 1) {
-    int v[3];
-    for (int k = 0; k < 3; ++k) v[k] = tid >= off ? s_scan[k][tid - off] : 0;
-    __syncthreads();
-    for (int k = 0; k < 3; ++k) s_scan[k][tid] += v[k];
-    __syncthreads();
-  }
-  int at = s_scan[0][tid] - own[0], slot = s_scan[1][tid] - own[1],
-      mi = s_scan[2][tid] - own[2];
-  for (int t = t0; t < t1; ++t) {
-    const int c = count[t];
-    for (int j = 0; j < c; ++j) {
-      piece_tile[at + j] = t;
-      piece_j[at + j] = j;
-    }
-    at += c;
-    if (c > 1) {
-      sbase[t] = slot;
-      slot += c;
-      multi_tile[mi++] = t;
-    } else {
-      sbase[t] = -1;
-    }
-  }
-  if (tid == PLAN_THREADS - 1) {
-    plan[0] = int32_t(P);
-    plan[1] = s_scan[0][tid];
-    plan[2] = s_scan[2][tid];
-    plan[3] = 0;
-  }
-}
-
 // ---------------------------------------------------------------- dQ reduce
 // dQ of a split row tile = scale * sum of its pieces' partials.  One workgroup per
 // (split row tile, KV head, 8-row group): its four 64-lane groups each add a fixed
@@ -1183,13 +1249,21 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   const int64_t n_q = int64_t(p.n_blocks) * p.block_size;
   const int64_t n_rows = n_q * p.n_q_heads;
   const int64_t n_ctx_tiles = (p.n_local + KV_KEYS - 1) / KV_KEYS;
+  const DqLayout l = bwd_dq_layout(p.n_blocks, p.block_size, p.n_q_heads, p.n_kv_heads);
+  const int64_t target = (kDqTargetWgs + p.n_kv_heads - 1) / p.n_kv_heads;
+  const int64_t q_grid = l.cap * p.n_kv_heads;
+  if (q_grid > 0x7fffffff || l.cap > 0x7fffffff || l.n_tiles > 0x7fffffff)
+    return hipErrorInvalidValue;
   {
+    const int64_t plan_wgs = l.n_tiles > 0 ? 1 : 0;
     const int64_t delta_wgs = (n_rows + (THREADS / 32) - 1) / (THREADS / 32);
     const int64_t seen_wgs = (n_ctx_tiles + THREADS - 1) / THREADS;
-    if (delta_wgs + seen_wgs > 0x7fffffff) return hipErrorInvalidValue;
-    if (delta_wgs + seen_wgs > 0) {
-      hipLaunchKernelGGL(bwd_delta_kernel, dim3(unsigned(delta_wgs + seen_wgs)), dim3(THREADS), 0,
-                         stream, p, n_rows, int(seen_wgs), int(n_ctx_tiles));
+    const int64_t grid = plan_wgs + seen_wgs + delta_wgs;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (grid > 0) {
+      hipLaunchKernelGGL(bwd_delta_kernel, dim3(unsigned(grid)), dim3(THREADS), 0, stream, p,
+                         n_rows, int(plan_wgs), int(seen_wgs), int(n_ctx_tiles), int(l.n_tiles),
+                         int(l.cap), int(target));
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -1204,18 +1278,10 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const DqLayout l = bwd_dq_layout(p.n_blocks, p.block_size, p.n_q_heads, p.n_kv_heads);
   if (l.n_tiles == 0) return hipSuccess;
-  const int64_t target = (kDqTargetWgs + p.n_kv_heads - 1) / p.n_kv_heads;
-  const int64_t q_grid = l.cap * p.n_kv_heads;
-  if (q_grid > 0x7fffffff || l.cap > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dq_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, p,
-                     int(l.n_tiles), int(l.cap), int(target));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(unsigned(q_grid)), dim3(THREADS), 0, stream, p,
                      int(l.n_tiles), int(l.cap));
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dq_reduce_kernel,
                      dim3(unsigned(l.n_tiles * p.n_kv_heads * (QROWS / RED_ROWS))), dim3(THREADS),

@@ -53,9 +53,13 @@ __global__ __launch_bounds__(kThreads) void fwd_order_kernel(FwdParams, int32_t*
   __shared__ int64_t s_blo[kRangeLdsBlocks], s_bhi[kRangeLdsBlocks];
   // the chunk table and every block's visible range, copied to LDS when they fit (one
   // round trip; every lane walks them below)
+  // (a table in the kernel arguments is copied whole, so the copy need not wait for
+  // the entry count: one round trip instead of two)
   const char* table = p.table.dev ? p.table.dev : (const char*)(p.table.words);
+  static_assert(kInlineBytes <= int(sizeof(s_table)), "an inline table fits the LDS copy");
   const int64_t table_bytes =
-      p.entries_off + int64_t(reinterpret_cast<const int32_t*>(table)[p.n_slots]) * 16;
+      p.table.dev ? p.entries_off + int64_t(reinterpret_cast<const int32_t*>(table)[p.n_slots]) * 16
+                  : kInlineBytes;
   const bool lds_table = table_bytes <= int64_t(sizeof(s_table));
   const bool lds_ranges = p.n_blocks <= kRangeLdsBlocks;
   if (lds_table) {
