@@ -1184,7 +1184,8 @@ __global__ __launch_bounds__(THREADS, 2) void bwd_dq_kernel(BwdParams, int n_til
 // (split row tile, KV head, 8-row group): its four 64-lane groups each add a fixed
 // quarter of the pieces in piece order, and the four sums are added in group order,
 // so the result is deterministic.  A long walk splits into many pieces (tens), and
-// one lane adding all of them one after another would set the kernel's time.
+// one lane adding all of them one after another would set the kernel's time.  Each
+// load instruction of a lane group reads 1 KB contiguous (two rows, 16 bytes a lane).
 constexpr int RED_ROWS = 8;
 constexpr int RED_SPLIT = THREADS / (RED_ROWS * 8);  // lane groups per row group
 
@@ -1204,22 +1205,22 @@ __global__ __launch_bounds__(THREADS) void bwd_dq_reduce_kernel(BwdParams, int n
   const int32_t* multi_tile = sbase + n_tiles + 2 * int64_t(cap);
   const int t = multi_tile[m];
   const int c = count[t], s0 = sbase[t];
-  const int k = threadIdx.x / (RED_ROWS * 8);  // lane group: pieces [c k / 4, c (k + 1) / 4)
-  const int li = threadIdx.x % (RED_ROWS * 8);
-  const int row = rg * RED_ROWS + (li >> 3), d0 = (li & 7) * 16;
-  const int64_t r = int64_t(t) * QROWS + row;
+  const int k = threadIdx.x >> 6;  // lane group: pieces [c k / 4, c (k + 1) / 4)
+  const int li = threadIdx.x & 63;
+  const int c4 = (li & 31) * 4;     // dims c4 .. c4 + 3 of rows 2 i + li / 32 (i < 4)
   const int64_t n_rows = int64_t(p.n_blocks) * p.block_size * G;
-  const bool row_ok = r < n_rows;
+  const int64_t rbase = int64_t(t) * QROWS + rg * RED_ROWS;
   f32x4v acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
   const int j0 = c * k / RED_SPLIT, j1 = c * (k + 1) / RED_SPLIT;
-  if (row_ok) {
-    for (int j = j0; j < j1; ++j) {
-      const float* src = p.dq_part + ((int64_t(s0 + j) * Hkv + g) * QROWS + row) * D + d0;
+  for (int j = j0; j < j1; ++j) {
+    const float* src = p.dq_part + ((int64_t(s0 + j) * Hkv + g) * QROWS + rg * RED_ROWS) * D + c4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i] += __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(src) + i);
+    for (int i = 0; i < 4; ++i) {
+      const int row = 2 * i + (li >> 5);
+      if (rbase + row < n_rows)
+        acc[i] += __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(src + row * D));
     }
   }
   if (k > 0) {
@@ -1227,19 +1228,21 @@ __global__ __launch_bounds__(THREADS) void bwd_dq_reduce_kernel(BwdParams, int n
     for (int i = 0; i < 4; ++i) s_part[k - 1][i][li] = acc[i];
   }
   __syncthreads();
-  if (k > 0 || !row_ok) return;
+  if (k > 0) return;
 #pragma unroll
   for (int q = 0; q < RED_SPLIT - 1; ++q)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += s_part[q][i][li];
-  const int64_t qi = r / G;
-  const int h = g * G + int(r % G);
-  float* dst = p.dq + (qi * Hq + h) * D + d0;
   const float sc = p.scale;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<float4*>(dst + 4 * i) =
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = rbase + 2 * i + (li >> 5);
+    if (r >= n_rows) continue;
+    const int64_t qi = r / G;
+    const int h = g * G + int(r % G);
+    *reinterpret_cast<float4*>(p.dq + (qi * Hq + h) * D + c4) =
         make_float4(acc[i].x * sc, acc[i].y * sc, acc[i].z * sc, acc[i].w * sc);
+  }
 }
 
 }  // namespace
