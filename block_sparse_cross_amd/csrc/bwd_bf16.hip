@@ -94,32 +94,36 @@ __device__ void dq_plan_workgroup(const BSX_KARG BwdParams& p, int n_tiles, int 
     const int64_t r1 = r0 + QROWS < n_rows ? r0 + QROWS : n_rows;
     row_span_union(p.anchor, p.ctx_begin, p.ctx_len, p.block_size, G, false, r0, r1, mlo, mhi);
   };
+  // key tiles of the walk over the chunk list E cut to [lo, hi): a sorted, disjoint list
+  // is bisected to its first entry ending after lo and walked only while entries start
+  // before hi; any other list is walked whole
+  auto walk_len = [&](const ChunkEntry* E, int64_t lo, int64_t hi) -> int64_t {
+    if (!(lo < hi)) return 0;
+    if (p.entries_order < 2) return walk_tiles(E, 0, p.n_entries, lo, hi, KT);
+    int e = 0, b = p.n_entries;
+    while (e < b) {
+      const int mid = (e + b) >> 1;
+      if (E[mid].start + int64_t(E[mid].len) > lo) b = mid; else e = mid + 1;
+    }
+    int64_t w = 0;
+    for (; e < p.n_entries && E[e].start < hi; ++e) w += walk_tiles(E, e, e + 1, lo, hi, KT);
+    return w;
+  };
   int64_t wsum = 0;
-  const bool small = n_tiles <= PLAN_LDS_TILES && p.n_entries <= PLAN_LDS_ENTRIES;
+  const bool lds_ent = p.n_entries <= PLAN_LDS_ENTRIES;
+  if (lds_ent)
+    for (int e = tid; e < p.n_entries; e += THREADS) s.ent[e] = ent[e];
+  const bool small = n_tiles <= PLAN_LDS_TILES && lds_ent;
   if (small) {
     // small plan: ranges, entries and the walk lengths in LDS
-    for (int e = tid; e < p.n_entries; e += THREADS) s.ent[e] = ent[e];
     for (int t = tid; t < n_tiles; t += THREADS) {
       span(t, &s.lo[t], &s.hi[t]);
       s.tiles[t] = 0;
     }
     __syncthreads();
     if (p.entries_order >= 2) {
-      // sorted and disjoint: a row tile bisects to its first entry ending after its
-      // range starts and walks only the entries its range reaches
-      for (int t = tid; t < n_tiles; t += THREADS) {
-        const int64_t lo = s.lo[t], hi = s.hi[t];
-        if (!(lo < hi)) continue;
-        int e = 0, b = p.n_entries;
-        while (e < b) {
-          const int mid = (e + b) >> 1;
-          if (s.ent[mid].start + int64_t(s.ent[mid].len) > lo) b = mid; else e = mid + 1;
-        }
-        int64_t w = 0;
-        for (; e < p.n_entries && s.ent[e].start < hi; ++e)
-          w += walk_tiles(s.ent, e, e + 1, lo, hi, KT);
-        s.tiles[t] = int32_t(w);
-      }
+      for (int t = tid; t < n_tiles; t += THREADS)
+        s.tiles[t] = int32_t(walk_len(s.ent, s.lo[t], s.hi[t]));
     } else {
       // (row tile, entry) pairs spread over all lanes (at most 2^18 of them here)
       const int n_pairs = n_tiles * p.n_entries;
@@ -132,10 +136,12 @@ __device__ void dq_plan_workgroup(const BSX_KARG BwdParams& p, int n_tiles, int 
     __syncthreads();
     for (int t = t0; t < t1; ++t) wsum += s.tiles[t];
   } else {
+    if (lds_ent) __syncthreads();  // the LDS copy of the list is complete
+    const ChunkEntry* E = lds_ent ? s.ent : ent;
     for (int t = t0; t < t1; ++t) {
       int64_t mlo, mhi;
       span(t, &mlo, &mhi);
-      const int64_t w = walk_tiles(ent, 0, p.n_entries, mlo, mhi, KT);
+      const int64_t w = walk_len(E, mlo, mhi);
       count[t] = int32_t(w < INT32_MAX ? w : INT32_MAX);
       wsum += w;
     }

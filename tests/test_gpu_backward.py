@@ -97,6 +97,16 @@ CASES = {
     # 2100 chunks of 2 keys: more entries than the dQ plan keeps in LDS
     "many_tiny_chunks": (4200, 4, 2, 4, [0, 4200, 2100, 1, 3333, 777], None,
                          list(range(0, 4200, 2)), [2] * 2100),
+    # the same past the LDS copy, listed out of position order: the plan walks the whole
+    # list from memory for every row tile
+    "many_chunks_unsorted": (2400, 4, 2, 4, [0, 2400, 1200, 7, 2399], None,
+                             [int(x) for x in np.random.default_rng(3).permutation(
+                                 np.arange(0, 2400, 4))], [4] * 600),
+    # 600 row tiles per KV head: more than the dQ plan keeps in LDS (the chunk list
+    # still fits there)
+    "plan_many_row_tiles": (512, 8, 2, 32,
+                            [int(x) for x in np.random.default_rng(7).integers(0, 513, 600)],
+                            None, [256, 0], [256, 256]),
 }
 
 
