@@ -13,7 +13,10 @@
 // exp(LSE_p - LSE) (0 for an empty partial); head_dim/4 lanes per row each own one
 // float4 column, and every lane accumulates kRowsPerThread rows at once, so each
 // partial is read as one contiguous piece of kRowsPerWg rows.  The loads of the next
-// kUnroll partials are issued before the current ones are consumed.
+// kUnroll partials are issued before the current ones are consumed.  A merge too small
+// to fill the chip twice over with 32-row workgroups (the training step's: 17 sets of
+// 32K rows) runs 16-row workgroups with four partials in flight per row instead: its
+// time is one workgroup's chain of dependent loads, not the memory system's rate.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -26,12 +29,8 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerThread = 4;
-constexpr int kRowsPerWg = 32;
-constexpr int kGroups = kThreads / kRowsPerWg;  // lane groups of phase 1
-constexpr int kUnroll = 2;                      // partials in flight per row
 constexpr int kPartsPerPass = kMergeBf16MaxParts;  // weights held in LDS at once
-static_assert(kThreads % kRowsPerWg == 0, "phase 1 needs whole lane groups");
+constexpr int64_t kSmallMergeWgs = 1024;  // 32-row workgroups in two rounds of four per CU
 
 __device__ inline f32x4 load_nt(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
@@ -53,13 +52,16 @@ __device__ inline void store_row(void* o_out, int64_t at, f32x4 v) {
 
 // kBf16: the merged O is written as bf16; launched only when one pass of weights covers
 // every partial (the f32 path adds later passes to the rows written so far).
-template <bool kBf16>
+// kRowsPerThread rows per lane, kRowsPerWg per workgroup, kUnroll partials in flight.
+template <bool kBf16, int kRowsPerThread, int kRowsPerWg, int kUnroll>
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_t n_rows,
                                                              int head_dim,
                                                              const float* __restrict__ o_parts,
                                                              const float* __restrict__ lse_parts,
                                                              void* __restrict__ o_out,
                                                              float* __restrict__ lse_out) {
+  constexpr int kGroups = kThreads / kRowsPerWg;  // lane groups of phase 1
+  static_assert(kThreads % kRowsPerWg == 0, "phase 1 needs whole lane groups");
   __shared__ float sh_m[kGroups][kRowsPerWg];
   __shared__ float sh_s[kGroups][kRowsPerWg];
   __shared__ float sh_lse[kRowsPerWg];
@@ -183,15 +185,22 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int n_parts, int64_
 hipError_t launch_lse_merge(int32_t n_parts, int64_t n_rows, int32_t head_dim,
                             const float* o_parts, const float* lse_parts, bool out_bf16,
                             void* o_out, float* lse_out, hipStream_t stream) {
-  const int64_t blocks = (n_rows + kRowsPerWg - 1) / kRowsPerWg;
-  if (out_bf16) {
-    if (n_parts > kPartsPerPass) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(lse_merge_kernel<true>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                       n_parts, n_rows, head_dim, o_parts, lse_parts, o_out, lse_out);
-  } else {
-    hipLaunchKernelGGL(lse_merge_kernel<false>, dim3(unsigned(blocks)), dim3(kThreads), 0,
-                       stream, n_parts, n_rows, head_dim, o_parts, lse_parts, o_out, lse_out);
-  }
+  if (out_bf16 && n_parts > kPartsPerPass) return hipErrorInvalidValue;
+  const bool small = (n_rows + 31) / 32 <= kSmallMergeWgs;
+  const int64_t blocks = small ? (n_rows + 15) / 16 : (n_rows + 31) / 32;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  if (small && out_bf16)
+    hipLaunchKernelGGL((lse_merge_kernel<true, 2, 16, 4>), grid, block, 0, stream, n_parts,
+                       n_rows, head_dim, o_parts, lse_parts, o_out, lse_out);
+  else if (small)
+    hipLaunchKernelGGL((lse_merge_kernel<false, 2, 16, 4>), grid, block, 0, stream, n_parts,
+                       n_rows, head_dim, o_parts, lse_parts, o_out, lse_out);
+  else if (out_bf16)
+    hipLaunchKernelGGL((lse_merge_kernel<true, 4, 32, 2>), grid, block, 0, stream, n_parts,
+                       n_rows, head_dim, o_parts, lse_parts, o_out, lse_out);
+  else
+    hipLaunchKernelGGL((lse_merge_kernel<false, 4, 32, 2>), grid, block, 0, stream, n_parts,
+                       n_rows, head_dim, o_parts, lse_parts, o_out, lse_out);
   return hipGetLastError();
 }
 
