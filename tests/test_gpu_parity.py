@@ -510,7 +510,8 @@ def test_merge_rank_sets_full_size_all_rows():
     record("64-set merge", n=n_rows, o=worst_o, lse=worst_l)
 
 
-@pytest.mark.parametrize("P,R", [(17, 512 * 32), (64, 1000), (128, 77)])
+# (the merge runs 16-row workgroups up to 32768 rows and 32-row ones above; both here)
+@pytest.mark.parametrize("P,R", [(17, 512 * 32), (64, 1000), (128, 77), (17, 40000)])
 def test_merge_bf16_output(P, R):
     """The bf16 merged output is the f32 merged output rounded to nearest even: bit-exact
     against the library's own f32 result rounded, and within one bf16 ulp (plus the f32
@@ -556,7 +557,8 @@ def test_merge_with_empty_partials():
     np.testing.assert_allclose(got_o[fin], ro[fin], atol=1e-5, rtol=0)
 
 
-@pytest.mark.parametrize("P,R,d", [(1, 5, 128), (3, 130, 64), (13, 77, 4), (2, 64, 512), (300, 40, 128)])
+@pytest.mark.parametrize("P,R,d", [(1, 5, 128), (3, 130, 64), (13, 77, 4), (2, 64, 512), (300, 40, 128),
+                                   (150, 33000, 4)])
 def test_merge_shapes(P, R, d):
     rng = np.random.default_rng(P * 1000 + R)
     o = rng.standard_normal((P, R, d)).astype(np.float32)
